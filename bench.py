@@ -1,0 +1,186 @@
+"""Throughput of the exact-attention prefill forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--no-cpu-baseline]
+
+One step is one fa_fwd call (the whole hot path: tile schedule, Q/K/V tile
+loads, S = QK^T, masking, online softmax, O += PV, epilogue) over the
+workload's synthetic inputs, which are resident in HBM before timing starts.
+Prints ONE JSON line.  ``value`` is TFLOP/s with the usual attention count
+4*b*h*sq*sk*d (halved when causal) over the wall-clock of the K timed steps;
+``roofline`` prices the kernel's average launch time (HIP events around each
+launch, on the stream the kernel runs on) against MI355X's dense bf16/fp16
+matrix peak; ``cpu_baseline`` times the fp64 oracle on a bounded sample of
+the same workload on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import workloads as W  # noqa: E402
+
+METRIC = "attn fwd TFLOP/s, b4 h32 sq4096 d128 bf16 causal; % of MFMA peak"
+# MI355X dense matrix peaks (TFLOP/s): 256 CUs x 2.4 GHz x FLOP/clk/CU
+PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}
+PEAK_HBM_GBS = 8000.0
+KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_86_amd", "csrc", f)
+                  for f in ("fa_fwd_kernels.hip", "fa_kernels.h", "fa_api.cpp")]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_sha() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_record(w: W.Workload):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s.json" % w.name)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_sha") != kernel_sha():
+        return None
+    return rec.get("traffic_bytes")
+
+
+def cpu_baseline(w: W.Workload, q, k, v, budget_s: float):
+    """Time the fp64 oracle on whole heads of the workload (about budget_s of
+    CPU work) and scale to TFLOP/s with the same FLOP convention."""
+    import oracle
+    nthreads = oracle.default_threads()
+    scale = float(np.float32(w.scale))
+    q64 = q[0:1, 0:1]
+    k64 = k[0:1, 0:1]
+    v64 = v[0:1, 0:1]
+    head_flops = w.flops / (w.b * w.h)
+    t0 = time.perf_counter()
+    oracle.attn(q64, k64, v64, scale, w.causal, nthreads=nthreads)
+    t1 = time.perf_counter() - t0
+    nheads = int(max(1, min(w.b * w.h - 1, budget_s / max(t1, 1e-3))))
+    # heads 1..nheads of the flattened [b*h] axis
+    qb = q.reshape(1, w.b * w.h, w.sq, w.d)[:, 1:1 + nheads]
+    kb = k.reshape(1, w.b * w.h, w.sk, w.d)[:, 1:1 + nheads]
+    vb = v.reshape(1, w.b * w.h, w.sk, w.d)[:, 1:1 + nheads]
+    t0 = time.perf_counter()
+    oracle.attn(qb, kb, vb, scale, w.causal, nthreads=nthreads)
+    dt = time.perf_counter() - t0
+    flops = head_flops * nheads
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": nthreads,
+            "kind": "oracle",
+            "sample": "%d of %d heads (full sq=%d x sk=%d each), fp64 C oracle, %.1f s" % (
+                nheads, w.b * w.h, w.sq, w.sk, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=W.HEADLINE.name, choices=sorted(W.BY_NAME))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: the forward pass is sharded over "
+              "heads with no exchange, so more GPUs add nothing to measure here; "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import exact_attention_86_amd as fa
+
+    w = W.BY_NAME[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log("[bench] generating %s" % w.name)
+    q, k, v = W.make(w)
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    od = torch.empty_like(qd)
+    lsed = torch.empty((w.b, w.h, w.sq), dtype=torch.float32, device=dev)
+    scale = float(np.float32(w.scale))
+    stream = torch.cuda.current_stream(dev)
+    code = W.DTYPE_CODE[w.dtype]
+    ptrs = (qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), od.data_ptr(), lsed.data_ptr())
+
+    def step():
+        rc = fa.fa_fwd(*ptrs, w.b, w.h, w.sq, w.sk, w.d, scale, int(w.causal), code,
+                       stream.cuda_stream)
+        if rc != fa.FA_OK:
+            raise fa.FaError(rc, fa.fa_last_error())
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # per-launch kernel time: HIP events on the launch stream around each call
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    evs[0].record(stream)
+    for i in range(args.steps):
+        step()
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)]
+    avg_ms = sum(per) / len(per)
+    ms_per_step = wall * 1e3 / args.steps
+
+    value = w.flops / (ms_per_step * 1e-3) / 1e12
+    achieved = w.flops / (avg_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    log("[bench] %s: wall %.3f ms/step, kernel avg %.3f ms (min %.3f, max %.3f), "
+        "%.1f TFLOP/s = %.1f%% of %.1f; %.0f GB/s algorithmic" % (
+            w.name, ms_per_step, avg_ms, min(per), max(per), achieved,
+            100 * achieved / peak, peak, w.algorithmic_bytes / (avg_ms * 1e-3) / 1e9))
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": dict(w.describe(), kernel="fa_fwd", parallelism="none (one GPU)"),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": traffic_record(w)},
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the oracle on a sample (~%.0f s)" % args.cpu_budget)
+        out["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_budget)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,128 @@
+"""Exact attention prefill forward for AMD MI355X (gfx950).
+
+Thin ctypes binding over the C ABI in ``include/fa.h`` (``libfa.so`` built
+in-tree by ``exact_attention_86_amd.build``).  The functions here only marshal
+arguments; every step of the computation runs in the library's HIP kernels.
+There is no CPU fallback: if the library is missing or fails to load, calls
+raise.
+
+    fa_fwd(q, k, v, o, lse, b, h, sq, sk, d, scale, causal, dtype, stream)
+        the C entry point with raw device addresses (ints) and sizes
+    attention(q, k, v, causal=False, scale=None, out=None, lse=None)
+        convenience wrapper over torch device tensors [b, h, s, d]
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libfa.so")
+
+FA_F32, FA_F16, FA_BF16 = 0, 1, 2
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_MISALIGNED, FA_ERR_TOO_LARGE, FA_ERR_HIP = range(6)
+STATUS_NAMES = {0: "FA_OK", 1: "FA_ERR_INVALID_ARG", 2: "FA_ERR_UNSUPPORTED",
+                3: "FA_ERR_MISALIGNED", 4: "FA_ERR_TOO_LARGE", 5: "FA_ERR_HIP"}
+DTYPE_CODES = {"f32": FA_F32, "f16": FA_F16, "bf16": FA_BF16}
+
+_lock = threading.Lock()
+_lib = None
+
+
+class FaError(RuntimeError):
+    """A non-zero status from the library."""
+
+    def __init__(self, code: int, msg: str):
+        super().__init__("%s: %s" % (STATUS_NAMES.get(code, str(code)), msg))
+        self.code = code
+
+
+def lib() -> ctypes.CDLL:
+    """Load libfa.so (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libfa.so is not built; run python -m exact_attention_86_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64 = ctypes.c_void_p, ctypes.c_int64
+        L.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                             ctypes.c_float, ctypes.c_int, ctypes.c_int, vp]
+        L.fa_fwd.restype = ctypes.c_int
+        ip = ctypes.POINTER(ctypes.c_int)
+        L.fa_query_config.argtypes = [ctypes.c_int, i64, ctypes.c_int, ip, ip, ip, ip]
+        L.fa_query_config.restype = ctypes.c_int
+        L.fa_last_error.argtypes = []
+        L.fa_last_error.restype = ctypes.c_char_p
+        L.fa_version.argtypes = []
+        L.fa_version.restype = ctypes.c_int
+        _lib = L
+        return L
+
+
+def fa_last_error() -> str:
+    return lib().fa_last_error().decode()
+
+
+def fa_version() -> int:
+    return lib().fa_version()
+
+
+def fa_query_config(dtype: int, d: int, causal: int = 0) -> dict:
+    vals = [ctypes.c_int(0) for _ in range(4)]
+    rc = lib().fa_query_config(int(dtype), int(d), int(causal), *[ctypes.byref(x) for x in vals])
+    if rc != FA_OK:
+        raise FaError(rc, fa_last_error())
+    return dict(zip(("block_m", "block_n", "waves", "lds"), (x.value for x in vals)))
+
+
+def fa_fwd(q, k, v, o, lse, b, h, sq, sk, d, scale, causal, dtype, stream) -> int:
+    """The C entry point: device addresses as ints, returns the status code."""
+    return lib().fa_fwd(q, k, v, o, lse, int(b), int(h), int(sq), int(sk), int(d),
+                        float(scale), int(causal), int(dtype), stream)
+
+
+def _dtype_code(t) -> int:
+    import torch
+    codes = {torch.float32: FA_F32, torch.float16: FA_F16, torch.bfloat16: FA_BF16}
+    if t.dtype not in codes:
+        raise FaError(FA_ERR_UNSUPPORTED, "dtype %s not served" % t.dtype)
+    return codes[t.dtype]
+
+
+def attention(q, k, v, causal: bool = False, scale: float | None = None, out=None,
+              lse=None, stream=None):
+    """O, LSE for torch device tensors q [b,h,sq,d], k/v [b,h,sk,d].
+
+    Outputs are allocated with torch when not given.  Runs on ``stream`` (a
+    torch stream) or torch's current stream; returns (O, LSE) without
+    synchronising.
+    """
+    import torch
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise FaError(FA_ERR_INVALID_ARG, "q, k, v must be 4-d [b, h, s, d]")
+    b, h, sq, d = q.shape
+    sk = k.shape[2]
+    if tuple(k.shape) != (b, h, sk, d) or tuple(v.shape) != (b, h, sk, d):
+        raise FaError(FA_ERR_INVALID_ARG, "k and v must be [b, h, sk, d] matching q")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise FaError(FA_ERR_INVALID_ARG, "q, k, v must be contiguous")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise FaError(FA_ERR_INVALID_ARG, "q, k, v must share a dtype")
+    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise FaError(FA_ERR_INVALID_ARG, "q, k, v must be device tensors")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((b, h, sq), dtype=torch.float32, device=q.device)
+    s = stream if stream is not None else torch.cuda.current_stream(q.device)
+    rc = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                b, h, sq, sk, d, scale, int(bool(causal)), _dtype_code(q), s.cuda_stream)
+    if rc != FA_OK:
+        raise FaError(rc, fa_last_error())
+    return out, lse

@@ -1,0 +1,120 @@
+// fa_api.cpp -- the C ABI of include/fa.h: argument checks, tiling, launch.
+//
+// Every check runs on the host before any HIP call, so an invalid call
+// enqueues nothing and the checks are testable on a machine without a GPU.
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "fa.h"
+#include "fa_kernels.h"
+
+namespace {
+
+thread_local char g_err[256] = "";
+
+int fail(int code, const char* msg)
+{
+    snprintf(g_err, sizeof g_err, "%s", msg);
+    return code;
+}
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb)
+{
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + nb && b0 < a0 + na;
+}
+
+}  // namespace
+
+extern "C" {
+
+FA_API const char* fa_last_error(void) { return g_err; }
+
+FA_API int fa_version(void) { return 100; /* 0.1.0 */ }
+
+FA_API int fa_query_config(int dtype, int64_t d, int causal, int* block_m, int* block_n,
+                           int* waves, int* lds)
+{
+    (void)causal;
+    fa::TileConfig tc;
+    if (d <= 0 || d > 4096 || !fa::tile_config(dtype, (int)d, &tc))
+        return fail(FA_ERR_UNSUPPORTED, "fa_query_config: dtype/head size not served");
+    if (block_m) *block_m = tc.block_m;
+    if (block_n) *block_n = tc.block_n;
+    if (waves) *waves = tc.waves;
+    if (lds) *lds = tc.lds;
+    g_err[0] = 0;
+    return FA_OK;
+}
+
+FA_API int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                  int64_t b, int64_t h, int64_t sq, int64_t sk, int64_t d, float scale,
+                  int causal, int dtype, void* stream)
+{
+    if (!q || !k || !v || !o || !lse)
+        return fail(FA_ERR_INVALID_ARG, "fa_fwd: NULL pointer");
+    if (b <= 0 || h <= 0 || sq <= 0 || sk <= 0 || d <= 0)
+        return fail(FA_ERR_INVALID_ARG, "fa_fwd: b, h, sq, sk and d must be >= 1");
+    if (!isfinite(scale))
+        return fail(FA_ERR_INVALID_ARG, "fa_fwd: scale must be finite");
+    if (causal != 0 && causal != 1)
+        return fail(FA_ERR_INVALID_ARG, "fa_fwd: causal must be 0 or 1");
+    if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16)
+        return fail(FA_ERR_UNSUPPORTED, "fa_fwd: unknown dtype");
+    fa::TileConfig tc;
+    if (d > 4096 || !fa::tile_config(dtype, (int)d, &tc))
+        return fail(FA_ERR_UNSUPPORTED, "fa_fwd: head size not served for this dtype");
+    if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u)
+        return fail(FA_ERR_MISALIGNED, "fa_fwd: q, k, v, o must be 16-byte aligned");
+    if ((uintptr_t)lse & 3u)
+        return fail(FA_ERR_MISALIGNED, "fa_fwd: lse must be 4-byte aligned");
+
+    // per-head slices use 32-bit offsets; head counts and the grid are int32
+    const int64_t lim = INT32_MAX;
+    if (sq * d > lim || sk * d > lim || b * h > lim || b > lim || h > lim)
+        return fail(FA_ERR_TOO_LARGE, "fa_fwd: a per-head slice exceeds 2^31-1 elements");
+    const int64_t n_mtiles = (sq + tc.block_m - 1) / tc.block_m;
+    const int64_t n_tiles = b * h * n_mtiles;
+    if (n_tiles > lim - 8)
+        return fail(FA_ERR_TOO_LARGE, "fa_fwd: too many tiles for one launch");
+
+    const size_t esz = dtype == FA_F32 ? 4 : 2;
+    const size_t nq = (size_t)(b * h * sq * d) * esz, nk = (size_t)(b * h * sk * d) * esz;
+    const size_t nl = (size_t)(b * h * sq) * 4;
+    if (overlap(o, nq, q, nq) || overlap(o, nq, k, nk) || overlap(o, nq, v, nk) ||
+        overlap(lse, nl, q, nq) || overlap(lse, nl, k, nk) || overlap(lse, nl, v, nk) ||
+        overlap(lse, nl, o, nq))
+        return fail(FA_ERR_INVALID_ARG, "fa_fwd: o and lse must not overlap the inputs or each other");
+
+    fa::Params p;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.o = o;
+    p.lse = lse;
+    p.bh = (int)(b * h);
+    p.sq = (int)sq;
+    p.sk = (int)sk;
+    // exponent factor in log2 units; a zero scale keeps a tiny positive factor
+    // so masked (-inf) scores still map to exp2(-inf) = 0 and every live score
+    // gives exp2(0 +- 1e-30 |s|) = 1 exactly in fp32
+    const float a = fabsf(scale);
+    p.c = a > 0.f ? (float)((double)a * 1.4426950408889634) : 1e-30f;
+    p.qsign = scale < 0.f ? (dtype == FA_F32 ? 1u : 0x80008000u) : 0u;
+    p.causal = causal;
+    p.n_mtiles = (int)n_mtiles;
+    p.n_tiles = (int)n_tiles;
+    p.grid = (int)(((n_tiles + 7) / 8) * 8);
+
+    hipError_t e = fa::launch_fwd(dtype, (int)d, p, (hipStream_t)stream);
+    if (e != hipSuccess) {
+        snprintf(g_err, sizeof g_err, "fa_fwd: launch failed: %s", hipGetErrorString(e));
+        return FA_ERR_HIP;
+    }
+    g_err[0] = 0;
+    return FA_OK;
+}
+
+}  // extern "C"

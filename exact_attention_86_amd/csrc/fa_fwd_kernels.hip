@@ -1,0 +1,589 @@
+// fa_fwd_kernels.hip -- exact attention prefill forward for gfx950 (CDNA4).
+//
+// Computes, per (batch, head) slice of contiguous [b, h, s, d] tensors,
+//   O = softmax(scale * Q K^T) V   and   LSE_i = ln sum_j exp(scale q_i.k_j)
+// (page "flash-attn 实现 prefill 阶段", section 问题分析), tile by tile with
+// the online softmax of page "flash.cu" (forward_kernel: a running row max m
+// and row sum l, rescaled per key tile), so the sq x sk score matrix never
+// reaches HBM.
+//
+// Design (one workgroup = one tile of BM query rows of one head):
+//  * NW waves of 64 lanes; wave w owns query rows [32w, 32w+32) of the tile,
+//    so a row's softmax never leaves its wave (page "05 · kernel 工程与四代演化",
+//    section 3, puts the warps of the FA2 traits along the query dimension).
+//  * Scores are computed transposed, S^T = K Q^T, on the 32x32 matrix cores:
+//    in the 32x32 accumulator layout lane l holds column l%32 -- one query --
+//    and 16 key rows, so the row max and row sum are in-lane reductions plus
+//    one exchange between the two 32-lane halves that share a query.
+//  * The output is accumulated transposed too, O^T += V^T P^T: P^T is the B
+//    operand straight from the score registers (no trip through LDS) and the
+//    per-query rescale factor is in-lane.  The key order the score layout
+//    imposes on P^T is matched by storing V^T in LDS with bits 2 and 3 of the
+//    key index swapped inside each 16-key group (a contraction does not care
+//    about the order of its summation index as long as both operands agree).
+//  * Q stays in registers for the whole key loop; K and V^T tiles are double
+//    buffered in LDS (padded rows against bank conflicts) and the next tile's
+//    global loads are issued before the current tile's math.
+//  * exp2 with the scale and log2(e) folded into one FMA; m is kept in log2
+//    units and converted back for LSE.
+//  * Causal: key tiles past a tile's last row are never loaded; a wave skips
+//    the math of key tiles that lie wholly above its own diagonal; masks are
+//    applied only on diagonal and ragged tiles.
+//  * Schedule: workgroup ids are mapped XCD-aware (consecutive ids land on
+//    different XCDs, so heads are grouped per XCD for L2 reuse of K/V) and,
+//    for causal, heaviest query tiles first within a head.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa_kernels.h"
+
+namespace fa {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies, 32 CUs each
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ f32x16_t mfma16(u32x4_t a, u32x4_t b, f32x16_t c, bool bf16)
+{
+    if (bf16)
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                       __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+}
+
+// two fp32 -> two 16-bit values packed in one dword, round-to-nearest-even
+__device__ __forceinline__ uint32_t pack2(float lo, float hi, bool bf16)
+{
+    if (bf16) {
+        typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+        bf16x2_t p;
+        p[0] = (__bf16)lo;
+        p[1] = (__bf16)hi;
+        return __builtin_bit_cast(uint32_t, p);
+    }
+    typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+    f16x2_t p;
+    p[0] = (_Float16)lo;
+    p[1] = (_Float16)hi;
+    return __builtin_bit_cast(uint32_t, p);
+}
+
+// workgroup id -> (head slice, query tile).  Consecutive workgroup ids are
+// dispatched round-robin over the XCDs; slot s of XCD x takes tile x*per + s
+// of the head-major tile order, so each XCD works through a contiguous run of
+// heads and its L2 sees the same K/V from many query tiles.
+__device__ __forceinline__ bool map_tile(const Params& p, int& bh, int& mt)
+{
+    const int id = blockIdx.x;
+    const int per = (p.n_tiles + kXcds - 1) / kXcds;
+    const int t = (id % kXcds) * per + id / kXcds;
+    if (t >= p.n_tiles) return false;
+    bh = t / p.n_mtiles;
+    const int r = t - bh * p.n_mtiles;
+    mt = p.causal ? p.n_mtiles - 1 - r : r;  // heaviest first when causal
+    return true;
+}
+
+// ---------------------------------------------------------------------------
+// 16-bit kernel (fp16 / bf16 on the 32x32x16 matrix cores)
+// ---------------------------------------------------------------------------
+template <int D, int BN, int NW, bool BF16, bool CAUSAL>
+__global__ void __launch_bounds__(NW * 64)
+fa_fwd_16(Params p)
+{
+    constexpr int BM = NW * 32;          // query rows per workgroup
+    constexpr int NT = NW * 64;          // threads
+    constexpr int NKB = BN / 32;         // 32-key blocks per key tile
+    constexpr int NDT = D / 32;          // 32-wide d tiles of the output
+    constexpr int NKK = D / 16;          // k-steps of the score product
+    constexpr int KS = D + 8;            // K row stride in LDS (elements)
+    constexpr int VS = BN + 8;           // V^T row stride in LDS (elements)
+    constexpr int KT = BN * KS;          // K tile (elements)
+    constexpr int VT = D * VS;           // V^T tile (elements)
+    constexpr int CPR = D / 8;           // 16-byte chunks per row
+    constexpr int KCH = BN * CPR / NT;   // K chunks per thread
+    constexpr int VUN = (BN / 4) * CPR / NT;  // V 4-key x 8-d units per thread
+    static_assert(KCH >= 1 && BN * CPR % NT == 0, "K tile must split evenly");
+    static_assert(VUN >= 1 && (BN / 4) * CPR % NT == 0, "V tile must split evenly");
+    static_assert(2 * (KT + VT) * 2 <= 160 * 1024, "LDS budget");
+
+    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * (KT + VT)];
+
+    int bh, mt;
+    if (!map_tile(p, bh, mt)) return;
+
+    const int tid = threadIdx.x;
+    const int w = tid >> 6;
+    const int lane = tid & 63;
+    const int l32 = lane & 31;
+    const int g = lane >> 5;
+
+    const int sq = p.sq, sk = p.sk;
+    const int q0 = mt * BM;
+    const uint16_t* __restrict__ Q = (const uint16_t*)p.q + (size_t)bh * sq * D;
+    const uint16_t* __restrict__ K = (const uint16_t*)p.k + (size_t)bh * sk * D;
+    const uint16_t* __restrict__ V = (const uint16_t*)p.v + (size_t)bh * sk * D;
+    uint16_t* __restrict__ O = (uint16_t*)p.o + (size_t)bh * sq * D;
+
+    // ---- Q fragment: B operand of S^T = K Q^T, lane = query, 8 d values ----
+    const int qrow = q0 + w * 32 + l32;
+    u32x4_t qf[NKK];
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+        if (qrow < sq) {
+            qf[kk] = *(const u32x4_t*)(Q + (size_t)qrow * D + kk * 16 + g * 8);
+            qf[kk] ^= p.qsign;
+        } else {
+            qf[kk] = u32x4_t{0, 0, 0, 0};
+        }
+    }
+
+    // ---- key range of this tile and of this wave ----
+    const int q_end = min(q0 + BM, sq);                 // one past the last live row
+    const int kv_end = CAUSAL ? min(q_end, sk) : sk;    // keys any row needs
+    const int nkv = (kv_end + BN - 1) / BN;
+    const int wq_first = q0 + w * 32;
+    const int wq_end = min(wq_first + 32, sq);
+    const int w_kv_end = (wq_end <= wq_first) ? 0 : (CAUSAL ? min(wq_end, sk) : sk);
+    const int w_nkv = (w_kv_end + BN - 1) / BN;
+
+    // ---- running softmax state (log2 units), output accumulator ----
+    float m_run = -INFINITY, l_run = 0.f;
+    f32x16_t oacc[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
+
+    // ---- global -> register staging of one K/V tile ----
+    u32x4_t kreg[KCH];
+    u32x4_t vreg[VUN][4];
+    auto load_tile = [&](int n0) {
+#pragma unroll
+        for (int i = 0; i < KCH; ++i) {
+            const int c = tid + i * NT;
+            const int row = c / CPR, col = c % CPR;
+            const int key = n0 + row;
+            kreg[i] = (key < sk) ? *(const u32x4_t*)(K + (size_t)key * D + col * 8)
+                                 : u32x4_t{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int i = 0; i < VUN; ++i) {
+            const int u = tid + i * NT;
+            const int kg = u % (BN / 4), dg = u / (BN / 4);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int key = n0 + kg * 4 + r;
+                vreg[i][r] = (key < sk) ? *(const u32x4_t*)(V + (size_t)key * D + dg * 8)
+                                        : u32x4_t{0, 0, 0, 0};
+            }
+        }
+    };
+    auto store_tile = [&](int buf) {
+        uint16_t* Ks = lds + buf * (KT + VT);
+        uint16_t* Vs = Ks + KT;
+#pragma unroll
+        for (int i = 0; i < KCH; ++i) {
+            const int c = tid + i * NT;
+            const int row = c / CPR, col = c % CPR;
+            *(u32x4_t*)(Ks + row * KS + col * 8) = kreg[i];
+        }
+#pragma unroll
+        for (int i = 0; i < VUN; ++i) {
+            const int u = tid + i * NT;
+            const int kg = u % (BN / 4), dg = u / (BN / 4);
+            // storage column of keys 4kg..4kg+3: swap bits 2,3 of the key offset
+            const int j = kg & 3;
+            const int col = (kg >> 2) * 16 + (((j & 1) << 1) | (j >> 1)) * 4;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int wd = e >> 1;
+                uint32_t a0 = vreg[i][0][wd], a1 = vreg[i][1][wd];
+                uint32_t a2 = vreg[i][2][wd], a3 = vreg[i][3][wd];
+                uint32_t lo, hi;
+                if (e & 1) {
+                    lo = (a0 >> 16) | (a1 & 0xffff0000u);
+                    hi = (a2 >> 16) | (a3 & 0xffff0000u);
+                } else {
+                    lo = (a0 & 0xffffu) | (a1 << 16);
+                    hi = (a2 & 0xffffu) | (a3 << 16);
+                }
+                *(u32x2_t*)(Vs + (dg * 8 + e) * VS + col) = u32x2_t{lo, hi};
+            }
+        }
+    };
+
+    const float c = p.c;  // |scale| * log2(e)
+
+    load_tile(0);
+    store_tile(0);
+    __syncthreads();
+
+    for (int t = 0; t < nkv; ++t) {
+        const int n0 = t * BN;
+        const bool more = (t + 1 < nkv);
+        if (more) load_tile(n0 + BN);
+
+        if (t < w_nkv) {
+            const uint16_t* Ks = lds + (t & 1) * (KT + VT);
+            const uint16_t* Vs = Ks + KT;
+
+            // ---- S^T = K Q^T on the matrix cores ----
+            f32x16_t s[NKB];
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+#pragma unroll
+                for (int kk = 0; kk < NKK; ++kk) {
+                    const u32x4_t a = *(const u32x4_t*)(Ks + (kb * 32 + l32) * KS + kk * 16 + g * 8);
+                    s[kb] = mfma16(a, qf[kk], s[kb], BF16);
+                }
+            }
+
+            // ---- masks: ragged key tail, causal diagonal ----
+            const bool need_mask = (n0 + BN > sk) || (CAUSAL && n0 + BN - 1 > wq_first);
+            if (need_mask) {
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int key = n0 + kb * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
+                        const bool dead = (key >= sk) || (CAUSAL && key > qrow);
+                        if (dead) s[kb][r] = -INFINITY;
+                    }
+            }
+
+            // ---- online softmax (log2 units) ----
+            float mx = s[0][0];
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float m_new = fmaxf(m_run, mx * c);
+            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+            const float alpha = fast_exp2(m_run - m_use);
+            m_run = m_new;
+
+            float lsum = 0.f;
+            uint32_t pk[NKB][8];
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; r += 2) {
+                    const float p0 = fast_exp2(__builtin_fmaf(s[kb][r], c, -m_use));
+                    const float p1 = fast_exp2(__builtin_fmaf(s[kb][r + 1], c, -m_use));
+                    lsum += p0 + p1;
+                    pk[kb][r >> 1] = pack2(p0, p1, BF16);
+                }
+            l_run = l_run * alpha + lsum;
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+
+            // ---- O^T += V^T P^T ----
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    const u32x4_t b = u32x4_t{pk[kb][half * 4 + 0], pk[kb][half * 4 + 1],
+                                              pk[kb][half * 4 + 2], pk[kb][half * 4 + 3]};
+#pragma unroll
+                    for (int dt = 0; dt < NDT; ++dt) {
+                        const u32x4_t a = *(const u32x4_t*)(Vs + (dt * 32 + l32) * VS + kb * 32 +
+                                                            half * 16 + g * 8);
+                        oacc[dt] = mfma16(a, b, oacc[dt], BF16);
+                    }
+                }
+        }
+
+        if (more) store_tile((t + 1) & 1);
+        __syncthreads();
+    }
+
+    // ---- epilogue: O = O^T / l, LSE = (m + log2 l) ln 2 ----
+    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    if (qrow < sq) {
+        const float inv = 1.f / l_tot;
+        uint16_t* orow = O + (size_t)qrow * D;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) {
+                const uint32_t w0 = pack2(oacc[dt][rb * 4 + 0] * inv, oacc[dt][rb * 4 + 1] * inv, BF16);
+                const uint32_t w1 = pack2(oacc[dt][rb * 4 + 2] * inv, oacc[dt][rb * 4 + 3] * inv, BF16);
+                *(u32x2_t*)(orow + dt * 32 + rb * 8 + g * 4) = u32x2_t{w0, w1};
+            }
+        if (g == 0) p.lse[(size_t)bh * sq + qrow] = (m_run + __log2f(l_tot)) * kLn2;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 kernel (32x32x2 fp32 matrix cores; probabilities stay fp32)
+// ---------------------------------------------------------------------------
+template <int D, int BN, int NW, bool CAUSAL>
+__global__ void __launch_bounds__(NW * 64)
+fa_fwd_32(Params p)
+{
+    constexpr int BM = NW * 32;
+    constexpr int NT = NW * 64;
+    constexpr int NKB = BN / 32;
+    constexpr int NDT = D / 32;
+    constexpr int NKK = D / 2;
+    constexpr int KS = D + 1;            // odd stride: rows land in distinct banks
+    constexpr int VS = D + 4;
+    constexpr int KT = BN * KS;
+    constexpr int VT = BN * VS;
+    constexpr int CPR = D / 4;           // 16-byte chunks per row
+    constexpr int CH = BN * CPR / NT;    // chunks per thread per tensor
+    static_assert(CH >= 1 && BN * CPR % NT == 0, "tile must split evenly");
+    static_assert(2 * (KT + VT) * 4 <= 160 * 1024, "LDS budget");
+
+    __shared__ __attribute__((aligned(16))) float lds[2 * (KT + VT)];
+
+    int bh, mt;
+    if (!map_tile(p, bh, mt)) return;
+
+    const int tid = threadIdx.x;
+    const int w = tid >> 6;
+    const int lane = tid & 63;
+    const int l32 = lane & 31;
+    const int g = lane >> 5;
+
+    const int sq = p.sq, sk = p.sk;
+    const int q0 = mt * BM;
+    const float* __restrict__ Q = (const float*)p.q + (size_t)bh * sq * D;
+    const float* __restrict__ K = (const float*)p.k + (size_t)bh * sk * D;
+    const float* __restrict__ V = (const float*)p.v + (size_t)bh * sk * D;
+    float* __restrict__ O = (float*)p.o + (size_t)bh * sq * D;
+
+    const int qrow = q0 + w * 32 + l32;
+    const float qs = p.qsign ? -1.f : 1.f;
+    float qf[NKK];
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk)
+        qf[kk] = (qrow < sq) ? qs * Q[(size_t)qrow * D + kk * 2 + g] : 0.f;
+
+    const int q_end = min(q0 + BM, sq);
+    const int kv_end = CAUSAL ? min(q_end, sk) : sk;
+    const int nkv = (kv_end + BN - 1) / BN;
+    const int wq_first = q0 + w * 32;
+    const int wq_end = min(wq_first + 32, sq);
+    const int w_kv_end = (wq_end <= wq_first) ? 0 : (CAUSAL ? min(wq_end, sk) : sk);
+    const int w_nkv = (w_kv_end + BN - 1) / BN;
+
+    float m_run = -INFINITY, l_run = 0.f;
+    f32x16_t oacc[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
+
+    typedef float f32x4_t __attribute__((ext_vector_type(4)));
+    f32x4_t kreg[CH], vreg[CH];
+    auto load_tile = [&](int n0) {
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            const int c = tid + i * NT;
+            const int row = c / CPR, col = c % CPR;
+            const int key = n0 + row;
+            const bool ok = key < sk;
+            kreg[i] = ok ? *(const f32x4_t*)(K + (size_t)key * D + col * 4) : f32x4_t{0, 0, 0, 0};
+            vreg[i] = ok ? *(const f32x4_t*)(V + (size_t)key * D + col * 4) : f32x4_t{0, 0, 0, 0};
+        }
+    };
+    auto store_tile = [&](int buf) {
+        float* Ks = lds + buf * (KT + VT);
+        float* Vs = Ks + KT;
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            const int c = tid + i * NT;
+            const int row = c / CPR, col = c % CPR;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Ks[row * KS + col * 4 + e] = kreg[i][e];
+            *(f32x4_t*)(Vs + row * VS + col * 4) = vreg[i];
+        }
+    };
+
+    const float c = p.c;
+
+    load_tile(0);
+    store_tile(0);
+    __syncthreads();
+
+    for (int t = 0; t < nkv; ++t) {
+        const int n0 = t * BN;
+        const bool more = (t + 1 < nkv);
+        if (more) load_tile(n0 + BN);
+
+        if (t < w_nkv) {
+            const float* Ks = lds + (t & 1) * (KT + VT);
+            const float* Vs = Ks + KT;
+
+            f32x16_t s[NKB];
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+#pragma unroll
+                for (int kk = 0; kk < NKK; ++kk) {
+                    const float a = Ks[(kb * 32 + l32) * KS + kk * 2 + g];
+                    s[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, qf[kk], s[kb], 0, 0, 0);
+                }
+            }
+
+            const bool need_mask = (n0 + BN > sk) || (CAUSAL && n0 + BN - 1 > wq_first);
+            if (need_mask) {
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int key = n0 + kb * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
+                        const bool dead = (key >= sk) || (CAUSAL && key > qrow);
+                        if (dead) s[kb][r] = -INFINITY;
+                    }
+            }
+
+            float mx = s[0][0];
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float m_new = fmaxf(m_run, mx * c);
+            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+            const float alpha = fast_exp2(m_run - m_use);
+            m_run = m_new;
+
+            float lsum = 0.f;
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float pr = fast_exp2(__builtin_fmaf(s[kb][r], c, -m_use));
+                    s[kb][r] = pr;
+                    lsum += pr;
+                }
+            l_run = l_run * alpha + lsum;
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+
+            // O^T += V^T P^T, one key per lane half per step: register r of
+            // block kb holds key kb*32 + 8(r/4) + 4g + r%4
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = kb * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
+#pragma unroll
+                    for (int dt = 0; dt < NDT; ++dt) {
+                        const float a = Vs[key * VS + dt * 32 + l32];
+                        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, s[kb][r], oacc[dt], 0, 0, 0);
+                    }
+                }
+        }
+
+        if (more) store_tile((t + 1) & 1);
+        __syncthreads();
+    }
+
+    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    if (qrow < sq) {
+        const float inv = 1.f / l_tot;
+        float* orow = O + (size_t)qrow * D;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) {
+                f32x4_t v4;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v4[e] = oacc[dt][rb * 4 + e] * inv;
+                *(f32x4_t*)(orow + dt * 32 + rb * 8 + g * 4) = v4;
+            }
+        if (g == 0) p.lse[(size_t)bh * sq + qrow] = (m_run + __log2f(l_tot)) * kLn2;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// launch table
+// ---------------------------------------------------------------------------
+template <typename KernelT>
+static hipError_t launch(KernelT kernel, int nw, const Params& p, hipStream_t stream)
+{
+    hipLaunchKernelGGL(kernel, dim3((unsigned)p.grid), dim3((unsigned)(nw * 64)), 0, stream, p);
+    return hipGetLastError();
+}
+
+template <int D, int BN, int NW, bool BF16>
+static hipError_t launch16(const Params& p, hipStream_t s)
+{
+    if (p.causal) return launch(fa_fwd_16<D, BN, NW, BF16, true>, NW, p, s);
+    return launch(fa_fwd_16<D, BN, NW, BF16, false>, NW, p, s);
+}
+
+template <int D, int BN, int NW>
+static hipError_t launch32(const Params& p, hipStream_t s)
+{
+    if (p.causal) return launch(fa_fwd_32<D, BN, NW, true>, NW, p, s);
+    return launch(fa_fwd_32<D, BN, NW, false>, NW, p, s);
+}
+
+// tile configuration per (dtype, d): keep in step with the launch table below
+bool tile_config(int dtype, int d, TileConfig* tc)
+{
+    int bn = 0, nw = 0, lds = 0;
+    if (dtype == 1 || dtype == 2) {
+        if (d == 64)       { bn = 128; nw = 4; }
+        else if (d == 128) { bn = 64; nw = 4; }
+        else if (d == 256) { bn = 32; nw = 4; }
+        else return false;
+        lds = 2 * (bn * (d + 8) + d * (bn + 8)) * 2;
+    } else if (dtype == 0) {
+        if (d == 64)       { bn = 32; nw = 2; }
+        else if (d == 128) { bn = 32; nw = 2; }
+        else return false;
+        lds = 2 * (bn * (d + 1) + bn * (d + 4)) * 4;
+    } else {
+        return false;
+    }
+    tc->block_m = nw * 32;
+    tc->block_n = bn;
+    tc->waves = nw;
+    tc->lds = lds;
+    return true;
+}
+
+hipError_t launch_fwd(int dtype, int d, const Params& p, hipStream_t s)
+{
+    switch (dtype) {
+    case 2:
+        if (d == 64) return launch16<64, 128, 4, true>(p, s);
+        if (d == 128) return launch16<128, 64, 4, true>(p, s);
+        if (d == 256) return launch16<256, 32, 4, true>(p, s);
+        break;
+    case 1:
+        if (d == 64) return launch16<64, 128, 4, false>(p, s);
+        if (d == 128) return launch16<128, 64, 4, false>(p, s);
+        if (d == 256) return launch16<256, 32, 4, false>(p, s);
+        break;
+    case 0:
+        if (d == 64) return launch32<64, 32, 2>(p, s);
+        if (d == 128) return launch32<128, 32, 2>(p, s);
+        break;
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace fa

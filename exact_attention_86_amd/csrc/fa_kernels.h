@@ -1,0 +1,34 @@
+// fa_kernels.h -- internal interface between the C ABI layer (fa_api.cpp) and
+// the gfx950 kernels (fa_fwd_kernels.hip).  Not installed, not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+// Launch parameters, passed by value as the kernel argument.
+struct Params {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;
+    int bh;          // b * h head slices
+    int sq, sk;      // sequence lengths
+    float c;         // |scale| * log2(e): exponent factor in log2 units
+    uint32_t qsign;  // 0x80008000 (16-bit) or 1 (fp32) when scale < 0: Q enters negated
+    int causal;      // 1: key j attends to query i iff j <= i
+    int n_mtiles;    // ceil(sq / block_m)
+    int n_tiles;     // bh * n_mtiles
+    int grid;        // workgroups launched
+};
+
+struct TileConfig {
+    int block_m, block_n, waves, lds;
+};
+
+bool tile_config(int dtype, int d, TileConfig* tc);
+hipError_t launch_fwd(int dtype, int d, const Params& p, hipStream_t stream);
+
+}  // namespace fa

@@ -1,0 +1,110 @@
+/*
+ * fa.h -- C ABI of the exact-attention prefill forward library for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The one operation: for every batch b and head h independently,
+ *
+ *     O   = softmax(scale * Q K^T) V                (rows of the softmax over keys)
+ *     LSE = log of the softmax denominator, per query row, natural-log units
+ *
+ * Page "flash-attn 实现 prefill 阶段", section 问题分析, states the formula
+ * and the [batch, heads, seq_len, head_dim] layout; page "flash.cu"
+ * (forward_kernel and forward) places the scale on the dot product before
+ * the exponential and keeps the running row max m and row sum l that make
+ * LSE = m + ln l.  Page "05 · kernel 工程与四代演化" (sections 2.1 and 6.1)
+ * names the causal variant and the forward entry point this library mirrors.
+ *
+ * Everything is asynchronous on the caller's HIP stream; the library keeps no
+ * state between calls and allocates no device memory.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define FA_API __attribute__((visibility("default")))
+#else
+#define FA_API
+#endif
+
+/* element types of q, k, v and o (lse is always fp32) */
+enum fa_dtype { FA_F32 = 0, FA_F16 = 1, FA_BF16 = 2 };
+
+/* return codes */
+enum fa_status {
+    FA_OK = 0,
+    FA_ERR_INVALID_ARG = 1, /* NULL pointer, size <= 0, non-finite scale,
+                               causal not 0/1, outputs overlapping inputs  */
+    FA_ERR_UNSUPPORTED = 2, /* unknown dtype, head size not served         */
+    FA_ERR_MISALIGNED = 3,  /* q, k, v, o not 16-byte aligned; lse not 4   */
+    FA_ERR_TOO_LARGE = 4,   /* a per-head slice or the grid exceeds 2^31-1 */
+    FA_ERR_HIP = 5          /* the HIP runtime refused the launch          */
+};
+
+/*
+ * fa_fwd -- exact attention prefill forward.
+ *
+ *   q      device pointer, [b, h, sq, d] contiguous row-major, dtype
+ *   k, v   device pointers, [b, h, sk, d] contiguous row-major, dtype
+ *   o      device pointer, [b, h, sq, d] contiguous row-major, dtype (output)
+ *   lse    device pointer, [b, h, sq] fp32 (output)
+ *   b, h   batch size and number of heads (>= 1)
+ *   sq, sk query and key sequence lengths (>= 1; need not be multiples of
+ *          any tile size)
+ *   d      head size: 64, 128 or 256 for FA_F16/FA_BF16; 64 or 128 for FA_F32
+ *   scale  multiplies q.k before the softmax (callers usually pass 1/sqrt(d));
+ *          any finite value
+ *   causal 0: every key attends; 1: query i attends to keys j <= i
+ *          (top-left alignment; the same as bottom-right when sq == sk)
+ *   dtype  FA_F32, FA_F16 or FA_BF16, shared by q, k, v and o
+ *   stream hipStream_t to enqueue on (NULL = the default stream)
+ *
+ * Numerics: dot products and the softmax run in fp32 with fp32 accumulation;
+ * for FA_F16/FA_BF16 the probabilities are rounded to the input type before
+ * they multiply V (the matrix units take 16-bit operands), while the row sum
+ * uses the unrounded fp32 values; for FA_F32 they stay fp32.  O is rounded to
+ * the output type with round-to-nearest-even.
+ *
+ * Ownership: the caller allocates and owns every buffer; o and lse must not
+ * overlap q, k, v or each other.  All argument checks happen on the host
+ * before any HIP call, so a failing call enqueues nothing.  The call returns
+ * after the launch is enqueued; faults during execution surface at the
+ * caller's next synchronisation.  Results are bitwise reproducible for a
+ * fixed device, shape and dtype (no atomics).
+ *
+ * Returns FA_OK or one of the fa_status codes; fa_last_error() then holds a
+ * message.
+ */
+FA_API int fa_fwd(const void* q, const void* k, const void* v, void* o,
+                  float* lse, int64_t b, int64_t h, int64_t sq, int64_t sk,
+                  int64_t d, float scale, int causal, int dtype, void* stream);
+
+/*
+ * fa_query_config -- the tiling fa_fwd uses for (dtype, d, causal).
+ *   block_m  query rows per workgroup tile
+ *   block_n  keys per inner step (one K/V tile through LDS)
+ *   waves    wavefronts per workgroup (64 lanes each)
+ *   lds      LDS bytes per workgroup
+ * Any output pointer may be NULL.  Returns FA_OK or FA_ERR_UNSUPPORTED.
+ * Host only; makes no HIP call.
+ */
+FA_API int fa_query_config(int dtype, int64_t d, int causal, int* block_m,
+                           int* block_n, int* waves, int* lds);
+
+/* fa_last_error -- message of the last failing call on this host thread
+ * ("" if none).  The pointer stays valid until the next call on the thread. */
+FA_API const char* fa_last_error(void);
+
+/* fa_version -- library version, major*10000 + minor*100 + patch. */
+FA_API int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

@@ -1,0 +1,124 @@
+"""The C ABI of include/fa.h, checked on the host (no GPU needed).
+
+The library must load on a machine without a GPU, export every symbol the
+header declares, and reject every invalid argument before it makes any HIP
+call.  No test here passes a combination that would reach a launch.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_attention_86_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+# fake, 16-byte aligned, non-overlapping device addresses: every call below
+# fails validation before it could use them
+A = 1 << 40
+Q, K, V, O, L = A, A + (1 << 34), A + (2 << 34), A + (3 << 34), A + (4 << 34)
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return re.findall(r"FA_API\s+[\w\s\*]+?\b(fa_\w+)\s*\(", text)
+
+
+def test_header_declares_the_entry_points():
+    assert set(declared_symbols()) == {"fa_fwd", "fa_query_config", "fa_last_error", "fa_version"}
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    L_ = fa.lib()
+    for name in declared_symbols():
+        assert hasattr(L_, name), name
+        assert ctypes.cast(getattr(L_, name), ctypes.c_void_p).value
+
+
+def test_version():
+    assert fa.fa_version() >= 100
+
+
+@pytest.mark.parametrize("dtype,d", [(fa.FA_F16, 64), (fa.FA_F16, 128), (fa.FA_F16, 256),
+                                     (fa.FA_BF16, 64), (fa.FA_BF16, 128), (fa.FA_BF16, 256),
+                                     (fa.FA_F32, 64), (fa.FA_F32, 128)])
+def test_query_config_served(dtype, d):
+    cfg = fa.fa_query_config(dtype, d, 1)
+    assert cfg["block_m"] == 32 * cfg["waves"]
+    assert cfg["block_n"] % 32 == 0
+    assert 0 < cfg["lds"] <= 160 * 1024
+
+
+@pytest.mark.parametrize("dtype,d", [(fa.FA_F32, 256), (fa.FA_BF16, 96), (fa.FA_BF16, 32),
+                                     (3, 128), (-1, 128), (fa.FA_F16, 0)])
+def test_query_config_unsupported(dtype, d):
+    with pytest.raises(fa.FaError) as e:
+        fa.fa_query_config(dtype, d, 0)
+    assert e.value.code == fa.FA_ERR_UNSUPPORTED
+
+
+def call(**kw):
+    args = dict(q=Q, k=K, v=V, o=O, lse=L, b=1, h=1, sq=16, sk=16, d=128,
+                scale=0.125, causal=0, dtype=fa.FA_BF16, stream=None)
+    args.update(kw)
+    return fa.fa_fwd(**args)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), fa.FA_ERR_INVALID_ARG),
+    (dict(k=0), fa.FA_ERR_INVALID_ARG),
+    (dict(v=0), fa.FA_ERR_INVALID_ARG),
+    (dict(o=0), fa.FA_ERR_INVALID_ARG),
+    (dict(lse=0), fa.FA_ERR_INVALID_ARG),
+    (dict(b=0), fa.FA_ERR_INVALID_ARG),
+    (dict(h=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(sq=0), fa.FA_ERR_INVALID_ARG),
+    (dict(sk=0), fa.FA_ERR_INVALID_ARG),
+    (dict(d=0), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), fa.FA_ERR_INVALID_ARG),
+    (dict(causal=2), fa.FA_ERR_INVALID_ARG),
+    (dict(causal=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(dtype=3), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=512), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=256, dtype=fa.FA_F32), fa.FA_ERR_UNSUPPORTED),
+    (dict(q=Q + 2), fa.FA_ERR_MISALIGNED),
+    (dict(k=K + 8), fa.FA_ERR_MISALIGNED),
+    (dict(v=V + 4), fa.FA_ERR_MISALIGNED),
+    (dict(o=O + 2), fa.FA_ERR_MISALIGNED),
+    (dict(lse=L + 2), fa.FA_ERR_MISALIGNED),
+    (dict(o=Q), fa.FA_ERR_INVALID_ARG),                       # o aliases q
+    (dict(o=K + 64), fa.FA_ERR_INVALID_ARG),                  # o inside k
+    (dict(lse=O + 1024), fa.FA_ERR_INVALID_ARG),              # lse inside o
+    (dict(lse=V), fa.FA_ERR_INVALID_ARG),                     # lse aliases v
+    (dict(sq=1 << 24, d=256), fa.FA_ERR_TOO_LARGE),           # sq*d = 2^32
+    (dict(sk=(1 << 31) // 64, d=64), fa.FA_ERR_TOO_LARGE),    # sk*d = 2^31
+    (dict(b=1 << 16, h=1 << 16, sq=1, sk=1), fa.FA_ERR_TOO_LARGE),  # b*h = 2^32
+])
+def test_invalid_arguments_rejected_before_launch(kw, code):
+    assert call(**kw) == code
+    assert fa.fa_last_error().startswith("fa_")
+
+
+def test_error_message_clears_on_success_path_query():
+    assert call(q=0) == fa.FA_ERR_INVALID_ARG
+    assert "NULL" in fa.fa_last_error()
+    fa.fa_query_config(fa.FA_BF16, 128, 0)
+    assert fa.fa_last_error() == ""
+
+
+def test_tensor_wrapper_rejects_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(fa.FaError):
+        fa.attention(x, x, x)
+
+
+def test_binding_has_no_cpu_fallback():
+    # the binding never imports the oracle or computes attention itself
+    src = open(os.path.join(ROOT, "exact_attention_86_amd", "__init__.py")).read()
+    assert "oracle" not in src
+    assert "torch.nn" not in src and "softmax" not in src and "matmul" not in src
