@@ -95,27 +95,54 @@ __device__ __forceinline__ bool map_tile(const Params& p, int& bh, int& mt)
 // ---------------------------------------------------------------------------
 // 16-bit kernel (fp16 / bf16 on the 32x32x16 matrix cores)
 // ---------------------------------------------------------------------------
+
+// XOR swizzle of the 16-byte chunks of a K/V row in LDS.  Physical chunk =
+// logical chunk ^ swz(row).  Eight consecutive rows read at one logical chunk
+// (the K operand pattern) and four consecutive rows read at a pair of chunks
+// (the transpose-read V pattern) both land in distinct LDS banks.
+__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+
+// LDS byte address of a pointer into a __shared__ array
+__device__ __forceinline__ uint32_t lds_addr(const void* ptr)
+{
+    return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) char*)ptr);
+}
+
+// One 1 KiB global -> LDS copy: lane i's 16 bytes at gptr land at LDS byte
+// address lds_base + 16 i.  Issued as inline assembly so the compiler does not
+// serialise later LDS reads of the other stage behind it; completion is
+// awaited explicitly with wait_copies() before the barrier that publishes it.
+__device__ __forceinline__ void copy_1k(const void* gptr, uint32_t lds_base)
+{
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :
+                 : "s"(lds_base), "v"(gptr)
+                 : "memory", "m0");
+}
+
+__device__ __forceinline__ void wait_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+
 template <int D, int BN, int NW, bool BF16, bool CAUSAL>
-__global__ void __launch_bounds__(NW * 64)
+__global__ void __launch_bounds__(NW * 64, 2)
 fa_fwd_16(Params p)
 {
     constexpr int BM = NW * 32;          // query rows per workgroup
-    constexpr int NT = NW * 64;          // threads
     constexpr int NKB = BN / 32;         // 32-key blocks per key tile
     constexpr int NDT = D / 32;          // 32-wide d tiles of the output
     constexpr int NKK = D / 16;          // k-steps of the score product
-    constexpr int KS = D + 8;            // K row stride in LDS (elements)
-    constexpr int VS = BN + 8;           // V^T row stride in LDS (elements)
-    constexpr int KT = BN * KS;          // K tile (elements)
-    constexpr int VT = D * VS;           // V^T tile (elements)
     constexpr int CPR = D / 8;           // 16-byte chunks per row
-    constexpr int KCH = BN * CPR / NT;   // K chunks per thread
-    constexpr int VUN = (BN / 4) * CPR / NT;  // V 4-key x 8-d units per thread
-    static_assert(KCH >= 1 && BN * CPR % NT == 0, "K tile must split evenly");
-    static_assert(VUN >= 1 && (BN / 4) * CPR % NT == 0, "V tile must split evenly");
-    static_assert(2 * (KT + VT) * 2 <= 160 * 1024, "LDS budget");
+    constexpr int TILE = BN * D;         // elements of one K or V tile
+    constexpr int NCH = BN * CPR;        // 16-byte chunks per tile
+    constexpr int DMA = NCH / 64 / NW;   // 1 KiB global->LDS copies per wave per tensor
+    static_assert(CPR >= 8, "swizzle needs at least 8 chunks per row");
+    static_assert(DMA >= 1 && NCH % (64 * NW) == 0, "tile must split evenly over waves");
+    static_assert(2 * 2 * TILE * 2 <= 160 * 1024, "LDS budget");
 
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * (KT + VT)];
+    // [stage][0 = K, 1 = V][BN rows x D], rows row-major with swizzled chunks
+    __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][TILE];
 
     int bh, mt;
     if (!map_tile(p, bh, mt)) return;
@@ -133,27 +160,53 @@ fa_fwd_16(Params p)
     const uint16_t* __restrict__ V = (const uint16_t*)p.v + (size_t)bh * sk * D;
     uint16_t* __restrict__ O = (uint16_t*)p.o + (size_t)bh * sq * D;
 
-    // ---- Q fragment: B operand of S^T = K Q^T, lane = query, 8 d values ----
-    const int qrow = q0 + w * 32 + l32;
-    u32x4_t qf[NKK];
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-        if (qrow < sq) {
-            qf[kk] = *(const u32x4_t*)(Q + (size_t)qrow * D + kk * 16 + g * 8);
-            qf[kk] ^= p.qsign;
-        } else {
-            qf[kk] = u32x4_t{0, 0, 0, 0};
-        }
-    }
-
     // ---- key range of this tile and of this wave ----
-    const int q_end = min(q0 + BM, sq);                 // one past the last live row
-    const int kv_end = CAUSAL ? min(q_end, sk) : sk;    // keys any row needs
+    const int q_end = min(q0 + BM, sq);
+    const int kv_end = CAUSAL ? min(q_end, sk) : sk;
     const int nkv = (kv_end + BN - 1) / BN;
     const int wq_first = q0 + w * 32;
     const int wq_end = min(wq_first + 32, sq);
     const int w_kv_end = (wq_end <= wq_first) ? 0 : (CAUSAL ? min(wq_end, sk) : sk);
     const int w_nkv = (w_kv_end + BN - 1) / BN;
+
+    // ---- global -> LDS copy of one K/V tile: lane i of copy j fills LDS
+    //      chunk c = (w*DMA + j)*64 + i, i.e. row c / CPR, physical chunk
+    //      c % CPR, fetched from logical chunk (c % CPR) ^ swz(row).  Rows past
+    //      the end are clamped to the last key (finite data; masked later). ----
+    auto issue_tile = [&](int n0, int stage) {
+#pragma unroll
+        for (int j = 0; j < DMA; ++j) {
+            const int c = (w * DMA + j) * 64 + lane;
+            const int row = c / CPR;
+            const int lch = (c % CPR) ^ swz(row);
+            const int key = min(n0 + row, sk - 1);
+            const size_t off = (size_t)key * D + lch * 8;
+            const int lbase = (w * DMA + j) * 64 * 8;
+            copy_1k(K + off, __builtin_amdgcn_readfirstlane(lds_addr(&lds[stage][0][lbase])));
+            copy_1k(V + off, __builtin_amdgcn_readfirstlane(lds_addr(&lds[stage][1][lbase])));
+        }
+    };
+
+    // first tile's copies go out before the Q loads
+    issue_tile(0, 0);
+
+    // ---- Q fragment: B operand of S^T = K Q^T, lane = query, 8 d values ----
+    // rows past the end read the last row (finite data, never stored)
+    const int qrow = q0 + w * 32 + l32;
+    const uint16_t* qptr = Q + (size_t)min(qrow, sq - 1) * D + g * 8;
+    u32x4_t qf[NKK];
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) qf[kk] = *(const u32x4_t*)(qptr + kk * 16) ^ p.qsign;
+
+    // per-lane LDS offsets (elements) of the operand reads
+    //  K (S^T A operand): row kb*32 + l32, logical chunk 2kk + g
+    const int k_row = l32;
+    const int k_h = g ^ swz(k_row);
+    //  V (O^T A operand via transpose reads): lane 4r + c of its 16-lane group
+    //  reads key row 16kc + 8j + 4g + r at d = 32dt + 16*half + 4c
+    const int sub = lane & 15, vr = sub >> 2, vc = sub & 3, vhalf = (lane >> 4) & 1;
+    const int v_row = 4 * g + vr;                 // + 16kc + 8j (multiples of 8)
+    const int v_f = swz(v_row);
 
     // ---- running softmax state (log2 units), output accumulator ----
     float m_run = -INFINITY, l_run = 0.f;
@@ -163,78 +216,18 @@ fa_fwd_16(Params p)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
 
-    // ---- global -> register staging of one K/V tile ----
-    u32x4_t kreg[KCH];
-    u32x4_t vreg[VUN][4];
-    auto load_tile = [&](int n0) {
-#pragma unroll
-        for (int i = 0; i < KCH; ++i) {
-            const int c = tid + i * NT;
-            const int row = c / CPR, col = c % CPR;
-            const int key = n0 + row;
-            kreg[i] = (key < sk) ? *(const u32x4_t*)(K + (size_t)key * D + col * 8)
-                                 : u32x4_t{0, 0, 0, 0};
-        }
-#pragma unroll
-        for (int i = 0; i < VUN; ++i) {
-            const int u = tid + i * NT;
-            const int kg = u % (BN / 4), dg = u / (BN / 4);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int key = n0 + kg * 4 + r;
-                vreg[i][r] = (key < sk) ? *(const u32x4_t*)(V + (size_t)key * D + dg * 8)
-                                        : u32x4_t{0, 0, 0, 0};
-            }
-        }
-    };
-    auto store_tile = [&](int buf) {
-        uint16_t* Ks = lds + buf * (KT + VT);
-        uint16_t* Vs = Ks + KT;
-#pragma unroll
-        for (int i = 0; i < KCH; ++i) {
-            const int c = tid + i * NT;
-            const int row = c / CPR, col = c % CPR;
-            *(u32x4_t*)(Ks + row * KS + col * 8) = kreg[i];
-        }
-#pragma unroll
-        for (int i = 0; i < VUN; ++i) {
-            const int u = tid + i * NT;
-            const int kg = u % (BN / 4), dg = u / (BN / 4);
-            // storage column of keys 4kg..4kg+3: swap bits 2,3 of the key offset
-            const int j = kg & 3;
-            const int col = (kg >> 2) * 16 + (((j & 1) << 1) | (j >> 1)) * 4;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int wd = e >> 1;
-                uint32_t a0 = vreg[i][0][wd], a1 = vreg[i][1][wd];
-                uint32_t a2 = vreg[i][2][wd], a3 = vreg[i][3][wd];
-                uint32_t lo, hi;
-                if (e & 1) {
-                    lo = (a0 >> 16) | (a1 & 0xffff0000u);
-                    hi = (a2 >> 16) | (a3 & 0xffff0000u);
-                } else {
-                    lo = (a0 & 0xffffu) | (a1 << 16);
-                    hi = (a2 & 0xffffu) | (a3 << 16);
-                }
-                *(u32x2_t*)(Vs + (dg * 8 + e) * VS + col) = u32x2_t{lo, hi};
-            }
-        }
-    };
-
     const float c = p.c;  // |scale| * log2(e)
-
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
+    constexpr float kRescaleThreshold = 8.f;  // lazy rescale: p <= 2^8
 
     for (int t = 0; t < nkv; ++t) {
         const int n0 = t * BN;
-        const bool more = (t + 1 < nkv);
-        if (more) load_tile(n0 + BN);
+        wait_copies();
+        __syncthreads();
+        if (t + 1 < nkv) issue_tile(n0 + BN, (t + 1) & 1);
 
         if (t < w_nkv) {
-            const uint16_t* Ks = lds + (t & 1) * (KT + VT);
-            const uint16_t* Vs = Ks + KT;
+            const uint16_t* Ks = lds[t & 1][0];
+            const uint16_t* Vs = lds[t & 1][1];
 
             // ---- S^T = K Q^T on the matrix cores ----
             f32x16_t s[NKB];
@@ -244,7 +237,8 @@ fa_fwd_16(Params p)
                 for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
 #pragma unroll
                 for (int kk = 0; kk < NKK; ++kk) {
-                    const u32x4_t a = *(const u32x4_t*)(Ks + (kb * 32 + l32) * KS + kk * 16 + g * 8);
+                    const int pch = (2 * kk) ^ k_h;
+                    const u32x4_t a = *(const u32x4_t*)(Ks + (kb * 32 + k_row) * D + pch * 8);
                     s[kb] = mfma16(a, qf[kk], s[kb], BF16);
                 }
             }
@@ -262,17 +256,26 @@ fa_fwd_16(Params p)
                     }
             }
 
-            // ---- online softmax (log2 units) ----
+            // ---- online softmax (log2 units) with lazy rescale ----
             float mx = s[0][0];
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float m_new = fmaxf(m_run, mx * c);
-            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-            const float alpha = fast_exp2(m_run - m_use);
-            m_run = m_new;
+            mx = fmaxf(mx, __shfl_xor(mx, 32));  // lanes l and l+32 share a query
+            const float mt_ = mx * c;
+            // rescale only when some row's max grew by more than 2^8
+            if (__builtin_amdgcn_ballot_w64(mt_ > m_run + kRescaleThreshold)) {
+                const float m_new = fmaxf(m_run, mt_);
+                const float alpha = fast_exp2(m_run - m_new);  // 0 when m_run = -inf
+                l_run *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+                m_run = m_new;
+            }
+            const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
 
             float lsum = 0.f;
             uint32_t pk[NKB][8];
@@ -285,30 +288,26 @@ fa_fwd_16(Params p)
                     lsum += p0 + p1;
                     pk[kb][r >> 1] = pack2(p0, p1, BF16);
                 }
-            l_run = l_run * alpha + lsum;
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+            l_run += lsum;
 
-            // ---- O^T += V^T P^T ----
+            // ---- O^T += V^T P^T: A operand = two 4-key transpose reads ----
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
+            for (int kc = 0; kc < 2 * NKB; ++kc) {
+                const u32x4_t b = u32x4_t{pk[kc >> 1][(kc & 1) * 4 + 0], pk[kc >> 1][(kc & 1) * 4 + 1],
+                                          pk[kc >> 1][(kc & 1) * 4 + 2], pk[kc >> 1][(kc & 1) * 4 + 3]};
 #pragma unroll
-                for (int half = 0; half < 2; ++half) {
-                    const u32x4_t b = u32x4_t{pk[kb][half * 4 + 0], pk[kb][half * 4 + 1],
-                                              pk[kb][half * 4 + 2], pk[kb][half * 4 + 3]};
-#pragma unroll
-                    for (int dt = 0; dt < NDT; ++dt) {
-                        const u32x4_t a = *(const u32x4_t*)(Vs + (dt * 32 + l32) * VS + kb * 32 +
-                                                            half * 16 + g * 8);
-                        oacc[dt] = mfma16(a, b, oacc[dt], BF16);
-                    }
+                for (int dt = 0; dt < NDT; ++dt) {
+                    const int lch = dt * 4 + 2 * vhalf + (vc >> 1);
+                    const int pch = lch ^ v_f;
+                    const int base = (16 * kc + v_row) * D + pch * 8 + (vc & 1) * 4;
+                    const v4i16_t x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(Vs + base));
+                    const v4i16_t x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(Vs + base + 8 * D));
+                    const u32x4_t a = u32x4_t{__builtin_bit_cast(u32x2_t, x0)[0], __builtin_bit_cast(u32x2_t, x0)[1],
+                                              __builtin_bit_cast(u32x2_t, x1)[0], __builtin_bit_cast(u32x2_t, x1)[1]};
+                    oacc[dt] = mfma16(a, b, oacc[dt], BF16);
                 }
+            }
         }
-
-        if (more) store_tile((t + 1) & 1);
-        __syncthreads();
     }
 
     // ---- epilogue: O = O^T / l, LSE = (m + log2 l) ln 2 ----

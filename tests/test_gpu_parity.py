@@ -179,6 +179,31 @@ def test_constant_v_and_one_hot(dt, gpu):
     assert float((lse.cpu() - 64.0).abs().max()) <= TOL_LSE
 
 
+@pytest.mark.parametrize("dt,d,sk", [("f16", 64, 64), ("f16", 128, 200), ("f16", 256, 100), ("bf16", 128, 300)])
+def test_one_hot_wide_score_range(dt, d, sk, gpu):
+    """Scores 64 (selected keys) vs 0 (others), scale 2: the row max lives in
+    one of the two lane halves that share a query, so a max exchange that
+    drops one half pushes fp16 probabilities past the fp16 range.  With
+    sk > d several keys share a column and O is the mean of their V rows."""
+    import torch
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16}[dt]
+    sq = 130
+    rng = np.random.default_rng(6)
+    col = rng.integers(0, min(sk, d), sq)
+    qn = np.zeros((1, 1, sq, d), np.float32)
+    qn[0, 0, np.arange(sq), col] = 1.0
+    kn = np.zeros((1, 1, sk, d), np.float32)
+    kn[0, 0, np.arange(sk), np.arange(sk) % d] = 32.0
+    vn = rng.standard_normal((1, 1, sk, d)).astype(np.float32)
+    q, k, v = (torch.from_numpy(x).to(tdt) for x in (qn, kn, vn))
+    o, lse = run_gpu(q, k, v, False, 2.0)
+    vr = v[0, 0].double().numpy()
+    ref = np.stack([vr[(np.arange(sk) % d) == col[i]].mean(0) for i in range(sq)])
+    cnt = np.array([np.sum((np.arange(sk) % d) == col[i]) for i in range(sq)])
+    assert float(np.abs(o[0, 0].double().cpu().numpy() - ref).max()) <= TOL_O[dt]
+    assert float(np.abs(lse[0, 0].double().cpu().numpy() - (64.0 + np.log(cnt))).max()) <= TOL_LSE
+
+
 def test_deterministic(gpu):
     import torch
     w = W.shape("det", "bf16", 2, 4, 777, 777, 128, True, seed=9)
