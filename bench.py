@@ -100,6 +100,9 @@ def main():
     ap.add_argument("--workload", default=W.HEADLINE.name, choices=sorted(W.BY_NAME))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="instead of attention, run a plain device-to-device copy of MIB MiB "
+                         "--steps times (reference for HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -114,6 +117,16 @@ def main():
     w = W.BY_NAME[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_launch": n, "launches": args.steps}), flush=True)
+        return
     log("[bench] generating %s" % w.name)
     q, k, v = W.make(w)
     qd, kd, vd = (t.to(dev) for t in (q, k, v))
