@@ -96,11 +96,22 @@ __device__ __forceinline__ bool map_tile(const Params& p, int& bh, int& mt)
 // 16-bit kernel (fp16 / bf16 on the 32x32x16 matrix cores)
 // ---------------------------------------------------------------------------
 
-// XOR swizzle of the 16-byte chunks of a K/V row in LDS.  Physical chunk =
-// logical chunk ^ swz(row).  Eight consecutive rows read at one logical chunk
-// (the K operand pattern) and four consecutive rows read at a pair of chunks
-// (the transpose-read V pattern) both land in distinct LDS banks.
-__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+// XOR swizzles of the 16-byte chunks of K and V rows in LDS (physical chunk =
+// logical chunk ^ swizzle(row)).  gfx950's LDS has 64 four-byte banks and
+// serves 16 lanes per clock, so a 16-byte K-operand read (16 lanes = 16
+// consecutive rows at one logical chunk) is conflict-free when the 16 rows map
+// to 16 distinct 16-byte bank groups: a bijection on the low four row bits
+// (three bits for 128-byte rows, whose row parity already picks the half of a
+// 256-byte bank line).  The V tile is read with 8-byte transpose reads, for
+// which the 8-row swizzle below measured fastest.
+template <int CPR>
+__device__ __forceinline__ int swz_k(int row)
+{
+    if (CPR >= 16)
+        return ((row & 1) ? 8 : 0) ^ ((row & 2) ? 2 : 0) ^ ((row & 4) ? 1 : 0) ^ ((row & 8) ? 4 : 0);
+    return ((row & 2) ? 4 : 0) ^ ((row & 4) ? 1 : 0) ^ ((row & 8) ? 2 : 0);
+}
+__device__ __forceinline__ int swz_v(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
 
 // LDS byte address of a pointer into a __shared__ array
 __device__ __forceinline__ uint32_t lds_addr(const void* ptr)
@@ -108,15 +119,15 @@ __device__ __forceinline__ uint32_t lds_addr(const void* ptr)
     return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) char*)ptr);
 }
 
-// One 1 KiB global -> LDS copy: lane i's 16 bytes at gptr land at LDS byte
-// address lds_base + 16 i.  Issued as inline assembly so the compiler does not
-// serialise later LDS reads of the other stage behind it; completion is
-// awaited explicitly with wait_copies() before the barrier that publishes it.
-__device__ __forceinline__ void copy_1k(const void* gptr, uint32_t lds_base)
+// One 1 KiB global -> LDS copy: lane i's 16 bytes at sbase + voff land at LDS
+// byte address lds_base + 16 i.  Issued as inline assembly so the compiler does
+// not serialise the other stage's LDS reads behind it; completion is awaited
+// explicitly with wait_copies() before the barrier that publishes the stage.
+__device__ __forceinline__ void copy_1k(const void* sbase, uint32_t voff, uint32_t lds_base)
 {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
                  :
-                 : "s"(lds_base), "v"(gptr)
+                 : "s"(lds_base), "v"(voff), "s"(sbase)
                  : "memory", "m0");
 }
 
@@ -124,6 +135,11 @@ __device__ __forceinline__ void wait_copies() { asm volatile("s_waitcnt vmcnt(0)
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+
+template <int S>
+struct Stage {
+    static constexpr int value = S;
+};
 
 template <int D, int BN, int NW, bool BF16, bool CAUSAL>
 __global__ void __launch_bounds__(NW * 64, 2)
@@ -134,12 +150,15 @@ fa_fwd_16(Params p)
     constexpr int NDT = D / 32;          // 32-wide d tiles of the output
     constexpr int NKK = D / 16;          // k-steps of the score product
     constexpr int CPR = D / 8;           // 16-byte chunks per row
+    constexpr int RB = D * 2;            // bytes per K/V row
     constexpr int TILE = BN * D;         // elements of one K or V tile
+    constexpr int TB = TILE * 2;         // bytes of one K or V tile
     constexpr int NCH = BN * CPR;        // 16-byte chunks per tile
-    constexpr int DMA = NCH / 64 / NW;   // 1 KiB global->LDS copies per wave per tensor
-    static_assert(CPR >= 8, "swizzle needs at least 8 chunks per row");
+    constexpr int DMA = NCH / 64 / NW;   // 1 KiB copies per wave per tensor per tile
+    constexpr int NKR = NKK < 8 ? NKK : 8;  // distinct K-read lane offsets
+    static_assert(CPR >= 8, "swizzles need at least 8 chunks per row");
     static_assert(DMA >= 1 && NCH % (64 * NW) == 0, "tile must split evenly over waves");
-    static_assert(2 * 2 * TILE * 2 <= 160 * 1024, "LDS budget");
+    static_assert(2 * 2 * TB <= 160 * 1024, "LDS budget");
 
     // [stage][0 = K, 1 = V][BN rows x D], rows row-major with swizzled chunks
     __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][TILE];
@@ -169,44 +188,66 @@ fa_fwd_16(Params p)
     const int w_kv_end = (wq_end <= wq_first) ? 0 : (CAUSAL ? min(wq_end, sk) : sk);
     const int w_nkv = (w_kv_end + BN - 1) / BN;
 
-    // ---- global -> LDS copy of one K/V tile: lane i of copy j fills LDS
-    //      chunk c = (w*DMA + j)*64 + i, i.e. row c / CPR, physical chunk
-    //      c % CPR, fetched from logical chunk (c % CPR) ^ swz(row).  Rows past
-    //      the end are clamped to the last key (finite data; masked later). ----
-    auto issue_tile = [&](int n0, int stage) {
-#pragma unroll
-        for (int j = 0; j < DMA; ++j) {
-            const int c = (w * DMA + j) * 64 + lane;
-            const int row = c / CPR;
-            const int lch = (c % CPR) ^ swz(row);
-            const int key = min(n0 + row, sk - 1);
-            const size_t off = (size_t)key * D + lch * 8;
-            const int lbase = (w * DMA + j) * 64 * 8;
-            copy_1k(K + off, __builtin_amdgcn_readfirstlane(lds_addr(&lds[stage][0][lbase])));
-            copy_1k(V + off, __builtin_amdgcn_readfirstlane(lds_addr(&lds[stage][1][lbase])));
-        }
-    };
-
-    // first tile's copies go out before the Q loads
-    issue_tile(0, 0);
-
-    // ---- Q fragment: B operand of S^T = K Q^T, lane = query, 8 d values ----
-    // rows past the end read the last row (finite data, never stored)
+    // ---- Q fragment: B operand of S^T = K Q^T, lane = query, 8 d values;
+    //      rows past the end read the last row (finite, never stored) ----
     const int qrow = q0 + w * 32 + l32;
     const uint16_t* qptr = Q + (size_t)min(qrow, sq - 1) * D + g * 8;
     u32x4_t qf[NKK];
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) qf[kk] = *(const u32x4_t*)(qptr + kk * 16) ^ p.qsign;
 
-    // per-lane LDS offsets (elements) of the operand reads
+    // ---- global -> LDS copies.  Copy j of wave w fills LDS chunks
+    //      c = (w*DMA + j)*64 + lane: row c / CPR, physical chunk c % CPR,
+    //      fetched from the swizzled logical chunk.  Per-lane byte offsets
+    //      within a tile are fixed; the tile base is a scalar. ----
+    uint32_t dk[DMA], dv[DMA];
+#pragma unroll
+    for (int j = 0; j < DMA; ++j) {
+        const int c = (w * DMA + j) * 64 + lane;
+        const int row = c / CPR, pch = c % CPR;
+        dk[j] = row * RB + ((pch ^ swz_k<CPR>(row)) << 4);
+        dv[j] = row * RB + ((pch ^ swz_v(row)) << 4);
+    }
+    const uint32_t lds0 = lds_addr(&lds[0][0][0]);
+    const uint32_t wofs = __builtin_amdgcn_readfirstlane(w * DMA * 1024);
+    auto issue_tile = [&](int n0, int stage) {
+        const uint16_t* kb = K + (size_t)n0 * D;
+        const uint16_t* vb = V + (size_t)n0 * D;
+        const uint32_t lk = lds0 + stage * 2 * TB + wofs;
+        if (n0 + BN <= sk) {
+#pragma unroll
+            for (int j = 0; j < DMA; ++j) {
+                copy_1k(kb, dk[j], lk + j * 1024);
+                copy_1k(vb, dv[j], lk + TB + j * 1024);
+            }
+        } else {
+            // ragged tail: rows past the last key re-read the last key (finite
+            // data; the scores of those keys are masked)
+            const int last = sk - 1 - n0;
+#pragma unroll
+            for (int j = 0; j < DMA; ++j) {
+                const int c = (w * DMA + j) * 64 + lane;
+                const int row = c / CPR, pch = c % CPR;
+                const int src = min(row, last);
+                copy_1k(kb, src * RB + ((pch ^ swz_k<CPR>(row)) << 4), lk + j * 1024);
+                copy_1k(vb, src * RB + ((pch ^ swz_v(row)) << 4), lk + TB + j * 1024);
+            }
+        }
+    };
+
+    // ---- per-lane LDS read offsets (bytes within a stage) ----
     //  K (S^T A operand): row kb*32 + l32, logical chunk 2kk + g
-    const int k_row = l32;
-    const int k_h = g ^ swz(k_row);
-    //  V (O^T A operand via transpose reads): lane 4r + c of its 16-lane group
-    //  reads key row 16kc + 8j + 4g + r at d = 32dt + 16*half + 4c
+    uint32_t rk[NKR];
+#pragma unroll
+    for (int kk = 0; kk < NKR; ++kk) rk[kk] = l32 * RB + (((2 * kk + g) ^ swz_k<CPR>(l32)) << 4);
+    //  V (O^T A operand, transpose reads): lane 4r + c of its 16-lane group
+    //  reads key row 16kc + 8j + 4g + r, d = 32dt + 16*half + 4c
     const int sub = lane & 15, vr = sub >> 2, vc = sub & 3, vhalf = (lane >> 4) & 1;
-    const int v_row = 4 * g + vr;                 // + 16kc + 8j (multiples of 8)
-    const int v_f = swz(v_row);
+    const int v_row = 4 * g + vr;
+    uint32_t rv[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+        rv[e] = TB + v_row * RB + (((e * 4 + 2 * vhalf + (vc >> 1)) ^ swz_v(v_row)) << 4) + (vc & 1) * 8;
 
     // ---- running softmax state (log2 units), output accumulator ----
     float m_run = -INFINITY, l_run = 0.f;
@@ -219,96 +260,105 @@ fa_fwd_16(Params p)
     const float c = p.c;  // |scale| * log2(e)
     constexpr float kRescaleThreshold = 8.f;  // lazy rescale: p <= 2^8
 
-    for (int t = 0; t < nkv; ++t) {
-        const int n0 = t * BN;
-        wait_copies();
-        __syncthreads();
-        if (t + 1 < nkv) issue_tile(n0 + BN, (t + 1) & 1);
+    auto compute = [&](auto stage_tag, int n0) {
+        constexpr int S = decltype(stage_tag)::value;
+        const char* sb = (const char*)&lds[S][0][0];
 
-        if (t < w_nkv) {
-            const uint16_t* Ks = lds[t & 1][0];
-            const uint16_t* Vs = lds[t & 1][1];
-
-            // ---- S^T = K Q^T on the matrix cores ----
-            f32x16_t s[NKB];
+        // ---- S^T = K Q^T on the matrix cores ----
+        f32x16_t s[NKB];
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) {
+        for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+            for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
 #pragma unroll
-                for (int kk = 0; kk < NKK; ++kk) {
-                    const int pch = (2 * kk) ^ k_h;
-                    const u32x4_t a = *(const u32x4_t*)(Ks + (kb * 32 + k_row) * D + pch * 8);
-                    s[kb] = mfma16(a, qf[kk], s[kb], BF16);
-                }
-            }
-
-            // ---- masks: ragged key tail, causal diagonal ----
-            const bool need_mask = (n0 + BN > sk) || (CAUSAL && n0 + BN - 1 > wq_first);
-            if (need_mask) {
-#pragma unroll
-                for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = n0 + kb * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
-                        const bool dead = (key >= sk) || (CAUSAL && key > qrow);
-                        if (dead) s[kb][r] = -INFINITY;
-                    }
-            }
-
-            // ---- online softmax (log2 units) with lazy rescale ----
-            float mx = s[0][0];
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-            mx = fmaxf(mx, __shfl_xor(mx, 32));  // lanes l and l+32 share a query
-            const float mt_ = mx * c;
-            // rescale only when some row's max grew by more than 2^8
-            if (__builtin_amdgcn_ballot_w64(mt_ > m_run + kRescaleThreshold)) {
-                const float m_new = fmaxf(m_run, mt_);
-                const float alpha = fast_exp2(m_run - m_new);  // 0 when m_run = -inf
-                l_run *= alpha;
-#pragma unroll
-                for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
-                m_run = m_new;
-            }
-            const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-
-            float lsum = 0.f;
-            uint32_t pk[NKB][8];
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; r += 2) {
-                    const float p0 = fast_exp2(__builtin_fmaf(s[kb][r], c, -m_use));
-                    const float p1 = fast_exp2(__builtin_fmaf(s[kb][r + 1], c, -m_use));
-                    lsum += p0 + p1;
-                    pk[kb][r >> 1] = pack2(p0, p1, BF16);
-                }
-            l_run += lsum;
-
-            // ---- O^T += V^T P^T: A operand = two 4-key transpose reads ----
-#pragma unroll
-            for (int kc = 0; kc < 2 * NKB; ++kc) {
-                const u32x4_t b = u32x4_t{pk[kc >> 1][(kc & 1) * 4 + 0], pk[kc >> 1][(kc & 1) * 4 + 1],
-                                          pk[kc >> 1][(kc & 1) * 4 + 2], pk[kc >> 1][(kc & 1) * 4 + 3]};
-#pragma unroll
-                for (int dt = 0; dt < NDT; ++dt) {
-                    const int lch = dt * 4 + 2 * vhalf + (vc >> 1);
-                    const int pch = lch ^ v_f;
-                    const int base = (16 * kc + v_row) * D + pch * 8 + (vc & 1) * 4;
-                    const v4i16_t x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(Vs + base));
-                    const v4i16_t x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(Vs + base + 8 * D));
-                    const u32x4_t a = u32x4_t{__builtin_bit_cast(u32x2_t, x0)[0], __builtin_bit_cast(u32x2_t, x0)[1],
-                                              __builtin_bit_cast(u32x2_t, x1)[0], __builtin_bit_cast(u32x2_t, x1)[1]};
-                    oacc[dt] = mfma16(a, b, oacc[dt], BF16);
-                }
+            for (int kk = 0; kk < NKK; ++kk) {
+                const u32x4_t a = *(const u32x4_t*)(sb + rk[kk & 7] + kb * 32 * RB + (kk >> 3) * 256);
+                s[kb] = mfma16(a, qf[kk], s[kb], BF16);
             }
         }
+
+        // ---- masks: ragged key tail, causal diagonal ----
+        const bool need_mask = (n0 + BN > sk) || (CAUSAL && n0 + BN - 1 > wq_first);
+        if (need_mask) {
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = n0 + kb * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
+                    const bool dead = (key >= sk) || (CAUSAL && key > qrow);
+                    if (dead) s[kb][r] = -INFINITY;
+                }
+        }
+
+        // ---- online softmax (log2 units) with lazy rescale ----
+        float mx = s[0][0];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));  // lanes l and l+32 share a query
+        const float mt_ = mx * c;
+        // rescale only when some row's max grew by more than 2^8
+        if (__builtin_amdgcn_ballot_w64(mt_ > m_run + kRescaleThreshold)) {
+            const float m_new = fmaxf(m_run, mt_);
+            const float alpha = fast_exp2(m_run - m_new);  // 0 when m_run = -inf
+            l_run *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+            m_run = m_new;
+        }
+        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+
+        float lsum = 0.f;
+        uint32_t pk[NKB][8];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+                const float p0 = fast_exp2(__builtin_fmaf(s[kb][r], c, -m_use));
+                const float p1 = fast_exp2(__builtin_fmaf(s[kb][r + 1], c, -m_use));
+                lsum += p0 + p1;
+                pk[kb][r >> 1] = pack2(p0, p1, BF16);
+            }
+        l_run += lsum;
+
+        // ---- O^T += V^T P^T: A operand = two 4-key transpose reads ----
+#pragma unroll
+        for (int kc = 0; kc < 2 * NKB; ++kc) {
+            const u32x4_t b = u32x4_t{pk[kc >> 1][(kc & 1) * 4 + 0], pk[kc >> 1][(kc & 1) * 4 + 1],
+                                      pk[kc >> 1][(kc & 1) * 4 + 2], pk[kc >> 1][(kc & 1) * 4 + 3]};
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) {
+                const char* va = sb + rv[dt & 1] + (dt >> 1) * 128 + kc * 16 * RB;
+                const v4i16_t x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(va));
+                const v4i16_t x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(va + 8 * RB));
+                const u32x4_t a = u32x4_t{__builtin_bit_cast(u32x2_t, x0)[0], __builtin_bit_cast(u32x2_t, x0)[1],
+                                          __builtin_bit_cast(u32x2_t, x1)[0], __builtin_bit_cast(u32x2_t, x1)[1]};
+                oacc[dt] = mfma16(a, b, oacc[dt], BF16);
+            }
+        }
+    };
+
+    // one key tile: publish its stage, prefetch the next tile into the other
+    // stage, then compute (stage index is a template constant so every LDS
+    // offset is an immediate)
+    auto step = [&](auto stage_tag, int t) {
+        constexpr int S = decltype(stage_tag)::value;
+        wait_copies();
+        __syncthreads();
+        if (t + 1 < nkv) issue_tile((t + 1) * BN, S ^ 1);
+        if (t < w_nkv) compute(stage_tag, t * BN);
+    };
+
+    issue_tile(0, 0);
+    int t = 0;
+    for (; t + 1 < nkv; t += 2) {
+        step(Stage<0>{}, t);
+        step(Stage<1>{}, t + 1);
     }
+    if (t < nkv) step(Stage<0>{}, t);
 
     // ---- epilogue: O = O^T / l, LSE = (m + log2 l) ln 2 ----
     const float l_tot = l_run + __shfl_xor(l_run, 32);
