@@ -75,9 +75,11 @@ FA_API int fa_fwd(const void* q, const void* k, const void* v, void* o, float* l
     const int64_t lim = INT32_MAX;
     if (sq * d > lim || sk * d > lim || b * h > lim || b > lim || h > lim)
         return fail(FA_ERR_TOO_LARGE, "fa_fwd: a per-head slice exceeds 2^31-1 elements");
+    // causal work items pair query tile nQ-1-i with tile i (equal cost)
     const int64_t n_mtiles = (sq + tc.block_m - 1) / tc.block_m;
-    const int64_t n_tiles = b * h * n_mtiles;
-    if (n_tiles > lim - 8)
+    const int64_t items_per_head = causal ? (n_mtiles + 1) / 2 : n_mtiles;
+    const int64_t n_items = b * h * items_per_head;
+    if (n_items > lim - 8)
         return fail(FA_ERR_TOO_LARGE, "fa_fwd: too many tiles for one launch");
 
     const size_t esz = dtype == FA_F32 ? 4 : 2;
@@ -105,8 +107,9 @@ FA_API int fa_fwd(const void* q, const void* k, const void* v, void* o, float* l
     p.qsign = scale < 0.f ? (dtype == FA_F32 ? 1u : 0x80008000u) : 0u;
     p.causal = causal;
     p.n_mtiles = (int)n_mtiles;
-    p.n_tiles = (int)n_tiles;
-    p.grid = (int)(((n_tiles + 7) / 8) * 8);
+    p.items_per_head = (int)items_per_head;
+    p.n_items = (int)n_items;
+    p.grid = (int)(((n_items + 7) / 8) * 8);
 
     hipError_t e = fa::launch_fwd(dtype, (int)d, p, (hipStream_t)stream);
     if (e != hipSuccess) {

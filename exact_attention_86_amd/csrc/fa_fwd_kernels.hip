@@ -76,20 +76,33 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi, bool bf16)
     return __builtin_bit_cast(uint32_t, p);
 }
 
-// workgroup id -> (head slice, query tile).  Consecutive workgroup ids are
-// dispatched round-robin over the XCDs; slot s of XCD x takes tile x*per + s
-// of the head-major tile order, so each XCD works through a contiguous run of
-// heads and its L2 sees the same K/V from many query tiles.
-__device__ __forceinline__ bool map_tile(const Params& p, int& bh, int& mt)
+// workgroup id -> (head slice, work item).  Consecutive workgroup ids are
+// dispatched round-robin over the XCDs; slot s of XCD x takes item x*per + s of
+// the head-major item order, so each XCD works through a contiguous run of
+// heads and its L2 sees the same K/V from many query tiles.  Causal items pair
+// query tile nQ-1-i (heaviest) with tile i (lightest), so every item costs
+// about nQ+1 key tiles and the grid drains without a long tail.
+__device__ __forceinline__ bool map_item(const Params& p, int& bh, int& item)
 {
     const int id = blockIdx.x;
-    const int per = (p.n_tiles + kXcds - 1) / kXcds;
+    const int per = (p.n_items + kXcds - 1) / kXcds;
     const int t = (id % kXcds) * per + id / kXcds;
-    if (t >= p.n_tiles) return false;
-    bh = t / p.n_mtiles;
-    const int r = t - bh * p.n_mtiles;
-    mt = p.causal ? p.n_mtiles - 1 - r : r;  // heaviest first when causal
+    if (t >= p.n_items) return false;
+    bh = t / p.items_per_head;
+    item = t - bh * p.items_per_head;
     return true;
+}
+
+// query tiles of a work item, heaviest first; returns how many (1 or 2)
+__device__ __forceinline__ int item_tiles(const Params& p, int item, int (&mt)[2])
+{
+    if (!p.causal) {
+        mt[0] = item;
+        return 1;
+    }
+    mt[0] = p.n_mtiles - 1 - item;
+    mt[1] = item;
+    return mt[0] == mt[1] ? 1 : 2;
 }
 
 // ---------------------------------------------------------------------------
@@ -163,8 +176,8 @@ fa_fwd_16(Params p)
     // [stage][0 = K, 1 = V][BN rows x D], rows row-major with swizzled chunks
     __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][TILE];
 
-    int bh, mt;
-    if (!map_tile(p, bh, mt)) return;
+    int bh, item;
+    if (!map_item(p, bh, item)) return;
 
     const int tid = threadIdx.x;
     const int w = tid >> 6;
@@ -173,207 +186,248 @@ fa_fwd_16(Params p)
     const int g = lane >> 5;
 
     const int sq = p.sq, sk = p.sk;
-    const int q0 = mt * BM;
-    const uint16_t* __restrict__ Q = (const uint16_t*)p.q + (size_t)bh * sq * D;
-    const uint16_t* __restrict__ K = (const uint16_t*)p.k + (size_t)bh * sk * D;
-    const uint16_t* __restrict__ V = (const uint16_t*)p.v + (size_t)bh * sk * D;
-    uint16_t* __restrict__ O = (uint16_t*)p.o + (size_t)bh * sq * D;
+    auto process = [&](const int mt) {
+        const int q0 = mt * BM;
+        const uint16_t* __restrict__ Q = (const uint16_t*)p.q + (size_t)bh * sq * D;
+        const uint16_t* __restrict__ K = (const uint16_t*)p.k + (size_t)bh * sk * D;
+        const uint16_t* __restrict__ V = (const uint16_t*)p.v + (size_t)bh * sk * D;
+        uint16_t* __restrict__ O = (uint16_t*)p.o + (size_t)bh * sq * D;
 
-    // ---- key range of this tile and of this wave ----
-    const int q_end = min(q0 + BM, sq);
-    const int kv_end = CAUSAL ? min(q_end, sk) : sk;
-    const int nkv = (kv_end + BN - 1) / BN;
-    const int wq_first = q0 + w * 32;
-    const int wq_end = min(wq_first + 32, sq);
-    const int w_kv_end = (wq_end <= wq_first) ? 0 : (CAUSAL ? min(wq_end, sk) : sk);
-    const int w_nkv = (w_kv_end + BN - 1) / BN;
+        // ---- key range of this tile and of this wave ----
+        const int q_end = min(q0 + BM, sq);
+        const int kv_end = CAUSAL ? min(q_end, sk) : sk;
+        const int nkv = (kv_end + BN - 1) / BN;
+        const int wq_first = q0 + w * 32;
+        const int wq_end = min(wq_first + 32, sq);
+        const int w_kv_end = (wq_end <= wq_first) ? 0 : (CAUSAL ? min(wq_end, sk) : sk);
+        const int w_nkv = (w_kv_end + BN - 1) / BN;
 
-    // ---- Q fragment: B operand of S^T = K Q^T, lane = query, 8 d values;
-    //      rows past the end read the last row (finite, never stored) ----
-    const int qrow = q0 + w * 32 + l32;
-    const uint16_t* qptr = Q + (size_t)min(qrow, sq - 1) * D + g * 8;
-    u32x4_t qf[NKK];
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) qf[kk] = *(const u32x4_t*)(qptr + kk * 16) ^ p.qsign;
+        // ---- Q fragment: B operand of S^T = K Q^T, lane = query, 8 d values;
+        //      rows past the end read the last row (finite, never stored) ----
+        const int qrow = q0 + w * 32 + l32;
+        const uint16_t* qptr = Q + (size_t)min(qrow, sq - 1) * D + g * 8;
+        u32x4_t qf[NKK];
+    #pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) qf[kk] = *(const u32x4_t*)(qptr + kk * 16) ^ p.qsign;
 
-    // ---- global -> LDS copies.  Copy j of wave w fills LDS chunks
-    //      c = (w*DMA + j)*64 + lane: row c / CPR, physical chunk c % CPR,
-    //      fetched from the swizzled logical chunk.  Per-lane byte offsets
-    //      within a tile are fixed; the tile base is a scalar. ----
-    uint32_t dk[DMA], dv[DMA];
-#pragma unroll
-    for (int j = 0; j < DMA; ++j) {
-        const int c = (w * DMA + j) * 64 + lane;
-        const int row = c / CPR, pch = c % CPR;
-        dk[j] = row * RB + ((pch ^ swz_k<CPR>(row)) << 4);
-        dv[j] = row * RB + ((pch ^ swz_v(row)) << 4);
-    }
-    const uint32_t lds0 = lds_addr(&lds[0][0][0]);
-    const uint32_t wofs = __builtin_amdgcn_readfirstlane(w * DMA * 1024);
-    auto issue_tile = [&](int n0, int stage) {
-        const uint16_t* kb = K + (size_t)n0 * D;
-        const uint16_t* vb = V + (size_t)n0 * D;
-        const uint32_t lk = lds0 + stage * 2 * TB + wofs;
-        if (n0 + BN <= sk) {
-#pragma unroll
-            for (int j = 0; j < DMA; ++j) {
-                copy_1k(kb, dk[j], lk + j * 1024);
-                copy_1k(vb, dv[j], lk + TB + j * 1024);
-            }
-        } else {
-            // ragged tail: rows past the last key re-read the last key (finite
-            // data; the scores of those keys are masked)
-            const int last = sk - 1 - n0;
-#pragma unroll
-            for (int j = 0; j < DMA; ++j) {
+        // ---- global -> LDS copies.  Copy j of wave w fills LDS chunks
+        //      c = (w*DMA + j)*64 + lane: row c / CPR, physical chunk c % CPR,
+        //      fetched from the swizzled logical chunk.  Per-lane byte offsets
+        //      within a tile are fixed; the tile base is a scalar. ----
+        uint32_t dk[DMA], dv[DMA];
+    #pragma unroll
+        for (int j = 0; j < DMA; ++j) {
+            const int c = (w * DMA + j) * 64 + lane;
+            const int row = c / CPR, pch = c % CPR;
+            dk[j] = row * RB + ((pch ^ swz_k<CPR>(row)) << 4);
+            dv[j] = row * RB + ((pch ^ swz_v(row)) << 4);
+        }
+        const uint32_t lds0 = lds_addr(&lds[0][0][0]);
+        const uint32_t wofs = __builtin_amdgcn_readfirstlane(w * DMA * 1024);
+        // copy j of K or V for the tile at n0 into stage `stage`.  FULL: the tile
+        // lies inside [0, sk) and the precomputed offsets apply; otherwise rows
+        // past the last key re-read the last key (finite data; those keys' scores
+        // are masked).
+        auto copy_k = [&](int j, int n0, int stage, bool full) {
+            const uint16_t* src = K + (size_t)n0 * D;
+            const uint32_t l = lds0 + stage * 2 * TB + wofs + j * 1024;
+            if (full) {
+                copy_1k(src, dk[j], l);
+            } else {
                 const int c = (w * DMA + j) * 64 + lane;
                 const int row = c / CPR, pch = c % CPR;
-                const int src = min(row, last);
-                copy_1k(kb, src * RB + ((pch ^ swz_k<CPR>(row)) << 4), lk + j * 1024);
-                copy_1k(vb, src * RB + ((pch ^ swz_v(row)) << 4), lk + TB + j * 1024);
+                copy_1k(src, min(row, sk - 1 - n0) * RB + ((pch ^ swz_k<CPR>(row)) << 4), l);
             }
-        }
-    };
-
-    // ---- per-lane LDS read offsets (bytes within a stage) ----
-    //  K (S^T A operand): row kb*32 + l32, logical chunk 2kk + g
-    uint32_t rk[NKR];
-#pragma unroll
-    for (int kk = 0; kk < NKR; ++kk) rk[kk] = l32 * RB + (((2 * kk + g) ^ swz_k<CPR>(l32)) << 4);
-    //  V (O^T A operand, transpose reads): lane 4r + c of its 16-lane group
-    //  reads key row 16kc + 8j + 4g + r, d = 32dt + 16*half + 4c
-    const int sub = lane & 15, vr = sub >> 2, vc = sub & 3, vhalf = (lane >> 4) & 1;
-    const int v_row = 4 * g + vr;
-    uint32_t rv[2];
-#pragma unroll
-    for (int e = 0; e < 2; ++e)
-        rv[e] = TB + v_row * RB + (((e * 4 + 2 * vhalf + (vc >> 1)) ^ swz_v(v_row)) << 4) + (vc & 1) * 8;
-
-    // ---- running softmax state (log2 units), output accumulator ----
-    float m_run = -INFINITY, l_run = 0.f;
-    f32x16_t oacc[NDT];
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
-
-    const float c = p.c;  // |scale| * log2(e)
-    constexpr float kRescaleThreshold = 8.f;  // lazy rescale: p <= 2^8
-
-    auto compute = [&](auto stage_tag, int n0) {
-        constexpr int S = decltype(stage_tag)::value;
-        const char* sb = (const char*)&lds[S][0][0];
-
-        // ---- S^T = K Q^T on the matrix cores ----
-        f32x16_t s[NKB];
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-#pragma unroll
-            for (int kk = 0; kk < NKK; ++kk) {
-                const u32x4_t a = *(const u32x4_t*)(sb + rk[kk & 7] + kb * 32 * RB + (kk >> 3) * 256);
-                s[kb] = mfma16(a, qf[kk], s[kb], BF16);
+        };
+        auto copy_v = [&](int j, int n0, int stage, bool full) {
+            const uint16_t* src = V + (size_t)n0 * D;
+            const uint32_t l = lds0 + stage * 2 * TB + TB + wofs + j * 1024;
+            if (full) {
+                copy_1k(src, dv[j], l);
+            } else {
+                const int c = (w * DMA + j) * 64 + lane;
+                const int row = c / CPR, pch = c % CPR;
+                copy_1k(src, min(row, sk - 1 - n0) * RB + ((pch ^ swz_v(row)) << 4), l);
             }
-        }
-
-        // ---- masks: ragged key tail, causal diagonal ----
-        const bool need_mask = (n0 + BN > sk) || (CAUSAL && n0 + BN - 1 > wq_first);
-        if (need_mask) {
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = n0 + kb * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
-                    const bool dead = (key >= sk) || (CAUSAL && key > qrow);
-                    if (dead) s[kb][r] = -INFINITY;
-                }
-        }
-
-        // ---- online softmax (log2 units) with lazy rescale ----
-        float mx = s[0][0];
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));  // lanes l and l+32 share a query
-        const float mt_ = mx * c;
-        // rescale only when some row's max grew by more than 2^8
-        if (__builtin_amdgcn_ballot_w64(mt_ > m_run + kRescaleThreshold)) {
-            const float m_new = fmaxf(m_run, mt_);
-            const float alpha = fast_exp2(m_run - m_new);  // 0 when m_run = -inf
-            l_run *= alpha;
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
-            m_run = m_new;
-        }
-        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-
-        float lsum = 0.f;
-        uint32_t pk[NKB][8];
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; r += 2) {
-                const float p0 = fast_exp2(__builtin_fmaf(s[kb][r], c, -m_use));
-                const float p1 = fast_exp2(__builtin_fmaf(s[kb][r + 1], c, -m_use));
-                lsum += p0 + p1;
-                pk[kb][r >> 1] = pack2(p0, p1, BF16);
+        };
+        auto issue_tile = [&](int n0, int stage) {
+            const bool full = n0 + BN <= sk;
+    #pragma unroll
+            for (int j = 0; j < DMA; ++j) {
+                copy_k(j, n0, stage, full);
+                copy_v(j, n0, stage, full);
             }
-        l_run += lsum;
+        };
+        // copies of the next tile are spread over the current tile's matrix-core
+        // work (K copies after each 32-key score block, V copies after each
+        // 16-key PV chunk) instead of one burst that stalls the wave at issue
+        constexpr int KC_PER = (DMA + NKB - 1) / NKB;
+        constexpr int VC_PER = (DMA + 2 * NKB - 1) / (2 * NKB);
 
-        // ---- O^T += V^T P^T: A operand = two 4-key transpose reads ----
-#pragma unroll
-        for (int kc = 0; kc < 2 * NKB; ++kc) {
-            const u32x4_t b = u32x4_t{pk[kc >> 1][(kc & 1) * 4 + 0], pk[kc >> 1][(kc & 1) * 4 + 1],
-                                      pk[kc >> 1][(kc & 1) * 4 + 2], pk[kc >> 1][(kc & 1) * 4 + 3]};
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) {
-                const char* va = sb + rv[dt & 1] + (dt >> 1) * 128 + kc * 16 * RB;
-                const v4i16_t x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(va));
-                const v4i16_t x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(va + 8 * RB));
-                const u32x4_t a = u32x4_t{__builtin_bit_cast(u32x2_t, x0)[0], __builtin_bit_cast(u32x2_t, x0)[1],
-                                          __builtin_bit_cast(u32x2_t, x1)[0], __builtin_bit_cast(u32x2_t, x1)[1]};
-                oacc[dt] = mfma16(a, b, oacc[dt], BF16);
-            }
-        }
-    };
+        // ---- per-lane LDS read offsets (bytes within a stage) ----
+        //  K (S^T A operand): row kb*32 + l32, logical chunk 2kk + g
+        uint32_t rk[NKR];
+    #pragma unroll
+        for (int kk = 0; kk < NKR; ++kk) rk[kk] = l32 * RB + (((2 * kk + g) ^ swz_k<CPR>(l32)) << 4);
+        //  V (O^T A operand, transpose reads): lane 4r + c of its 16-lane group
+        //  reads key row 16kc + 8j + 4g + r, d = 32dt + 16*half + 4c
+        const int sub = lane & 15, vr = sub >> 2, vc = sub & 3, vhalf = (lane >> 4) & 1;
+        const int v_row = 4 * g + vr;
+        uint32_t rv[2];
+    #pragma unroll
+        for (int e = 0; e < 2; ++e)
+            rv[e] = TB + v_row * RB + (((e * 4 + 2 * vhalf + (vc >> 1)) ^ swz_v(v_row)) << 4) + (vc & 1) * 8;
 
-    // one key tile: publish its stage, prefetch the next tile into the other
-    // stage, then compute (stage index is a template constant so every LDS
-    // offset is an immediate)
-    auto step = [&](auto stage_tag, int t) {
-        constexpr int S = decltype(stage_tag)::value;
-        wait_copies();
-        __syncthreads();
-        if (t + 1 < nkv) issue_tile((t + 1) * BN, S ^ 1);
-        if (t < w_nkv) compute(stage_tag, t * BN);
-    };
-
-    issue_tile(0, 0);
-    int t = 0;
-    for (; t + 1 < nkv; t += 2) {
-        step(Stage<0>{}, t);
-        step(Stage<1>{}, t + 1);
-    }
-    if (t < nkv) step(Stage<0>{}, t);
-
-    // ---- epilogue: O = O^T / l, LSE = (m + log2 l) ln 2 ----
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
-    if (qrow < sq) {
-        const float inv = 1.f / l_tot;
-        uint16_t* orow = O + (size_t)qrow * D;
-#pragma unroll
+        // ---- running softmax state (log2 units), output accumulator ----
+        float m_run = -INFINITY, l_run = 0.f;
+        f32x16_t oacc[NDT];
+    #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-            for (int rb = 0; rb < 4; ++rb) {
-                const uint32_t w0 = pack2(oacc[dt][rb * 4 + 0] * inv, oacc[dt][rb * 4 + 1] * inv, BF16);
-                const uint32_t w1 = pack2(oacc[dt][rb * 4 + 2] * inv, oacc[dt][rb * 4 + 3] * inv, BF16);
-                *(u32x2_t*)(orow + dt * 32 + rb * 8 + g * 4) = u32x2_t{w0, w1};
+    #pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
+
+        const float c = p.c;  // |scale| * log2(e)
+        constexpr float kRescaleThreshold = 8.f;  // lazy rescale: p <= 2^8
+
+        // PF_FULL: the next tile lies inside [0, sk) and its copies are issued
+        // from inside this tile's math; otherwise the caller has issued them
+        auto compute = [&](auto stage_tag, auto full_tag, int n0) {
+            constexpr int S = decltype(stage_tag)::value;
+            constexpr bool PF_FULL = decltype(full_tag)::value;
+            const char* sb = (const char*)&lds[S][0][0];
+            const int nn = n0 + BN;  // prefetched tile
+
+            // ---- S^T = K Q^T on the matrix cores ----
+            f32x16_t s[NKB];
+    #pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+    #pragma unroll
+                for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+    #pragma unroll
+                for (int kk = 0; kk < NKK; ++kk) {
+                    const u32x4_t a = *(const u32x4_t*)(sb + rk[kk & 7] + kb * 32 * RB + (kk >> 3) * 256);
+                    s[kb] = mfma16(a, qf[kk], s[kb], BF16);
+                }
+    #pragma unroll
+                for (int j = kb * KC_PER; j < (kb + 1) * KC_PER && j < DMA; ++j)
+                    if (PF_FULL) copy_k(j, nn, S ^ 1, true);
             }
-        if (g == 0) p.lse[(size_t)bh * sq + qrow] = (m_run + __log2f(l_tot)) * kLn2;
+
+            // ---- masks: ragged key tail, causal diagonal ----
+            const bool need_mask = (n0 + BN > sk) || (CAUSAL && n0 + BN - 1 > wq_first);
+            if (need_mask) {
+    #pragma unroll
+                for (int kb = 0; kb < NKB; ++kb)
+    #pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int key = n0 + kb * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
+                        const bool dead = (key >= sk) || (CAUSAL && key > qrow);
+                        if (dead) s[kb][r] = -INFINITY;
+                    }
+            }
+
+            // ---- online softmax (log2 units) with lazy rescale ----
+            float mx = s[0][0];
+    #pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+    #pragma unroll
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+            mx = fmaxf(mx, __shfl_xor(mx, 32));  // lanes l and l+32 share a query
+            const float mt_ = mx * c;
+            // rescale only when some row's max grew by more than 2^8
+            if (__builtin_amdgcn_ballot_w64(mt_ > m_run + kRescaleThreshold)) {
+                const float m_new = fmaxf(m_run, mt_);
+                const float alpha = fast_exp2(m_run - m_new);  // 0 when m_run = -inf
+                l_run *= alpha;
+    #pragma unroll
+                for (int dt = 0; dt < NDT; ++dt)
+    #pragma unroll
+                    for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+                m_run = m_new;
+            }
+            const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+
+            float lsum = 0.f;
+            uint32_t pk[NKB][8];
+    #pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+    #pragma unroll
+                for (int r = 0; r < 16; r += 2) {
+                    const float p0 = fast_exp2(__builtin_fmaf(s[kb][r], c, -m_use));
+                    const float p1 = fast_exp2(__builtin_fmaf(s[kb][r + 1], c, -m_use));
+                    lsum += p0 + p1;
+                    pk[kb][r >> 1] = pack2(p0, p1, BF16);
+                }
+            l_run += lsum;
+
+            // ---- O^T += V^T P^T: A operand = two 4-key transpose reads ----
+    #pragma unroll
+            for (int kc = 0; kc < 2 * NKB; ++kc) {
+                const u32x4_t b = u32x4_t{pk[kc >> 1][(kc & 1) * 4 + 0], pk[kc >> 1][(kc & 1) * 4 + 1],
+                                          pk[kc >> 1][(kc & 1) * 4 + 2], pk[kc >> 1][(kc & 1) * 4 + 3]};
+    #pragma unroll
+                for (int dt = 0; dt < NDT; ++dt) {
+                    const char* va = sb + rv[dt & 1] + (dt >> 1) * 128 + kc * 16 * RB;
+                    const v4i16_t x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(va));
+                    const v4i16_t x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(va + 8 * RB));
+                    const u32x4_t a = u32x4_t{__builtin_bit_cast(u32x2_t, x0)[0], __builtin_bit_cast(u32x2_t, x0)[1],
+                                              __builtin_bit_cast(u32x2_t, x1)[0], __builtin_bit_cast(u32x2_t, x1)[1]};
+                    oacc[dt] = mfma16(a, b, oacc[dt], BF16);
+                }
+    #pragma unroll
+                for (int j = kc * VC_PER; j < (kc + 1) * VC_PER && j < DMA; ++j)
+                    if (PF_FULL) copy_v(j, nn, S ^ 1, true);
+            }
+        };
+
+        // one key tile: publish its stage, prefetch the next tile into the other
+        // stage, then compute (stage index is a template constant so every LDS
+        // offset is an immediate)
+        auto step = [&](auto stage_tag, int t) {
+            constexpr int S = decltype(stage_tag)::value;
+            wait_copies();
+            __syncthreads();
+            const bool pf = t + 1 < nkv;
+            const bool pf_full = pf && (t + 2) * BN <= sk;
+            if (t < w_nkv && pf_full) {
+                compute(stage_tag, Stage<1>{}, t * BN);
+            } else {
+                if (pf) issue_tile((t + 1) * BN, S ^ 1);
+                if (t < w_nkv) compute(stage_tag, Stage<0>{}, t * BN);
+            }
+        };
+
+        issue_tile(0, 0);
+        int t = 0;
+        for (; t + 1 < nkv; t += 2) {
+            step(Stage<0>{}, t);
+            step(Stage<1>{}, t + 1);
+        }
+        if (t < nkv) step(Stage<0>{}, t);
+
+        // ---- epilogue: O = O^T / l, LSE = (m + log2 l) ln 2 ----
+        const float l_tot = l_run + __shfl_xor(l_run, 32);
+        if (qrow < sq) {
+            const float inv = 1.f / l_tot;
+            uint16_t* orow = O + (size_t)qrow * D;
+    #pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+    #pragma unroll
+                for (int rb = 0; rb < 4; ++rb) {
+                    const uint32_t w0 = pack2(oacc[dt][rb * 4 + 0] * inv, oacc[dt][rb * 4 + 1] * inv, BF16);
+                    const uint32_t w1 = pack2(oacc[dt][rb * 4 + 2] * inv, oacc[dt][rb * 4 + 3] * inv, BF16);
+                    *(u32x2_t*)(orow + dt * 32 + rb * 8 + g * 4) = u32x2_t{w0, w1};
+                }
+            if (g == 0) p.lse[(size_t)bh * sq + qrow] = (m_run + __log2f(l_tot)) * kLn2;
+        }
+    };
+
+    int mts[2];
+    const int nt = item_tiles(p, item, mts);
+    process(mts[0]);
+    if (nt > 1) {
+        __syncthreads();  // every wave is done with the LDS stages
+        process(mts[1]);
     }
 }
 
@@ -400,8 +454,8 @@ fa_fwd_32(Params p)
 
     __shared__ __attribute__((aligned(16))) float lds[2 * (KT + VT)];
 
-    int bh, mt;
-    if (!map_tile(p, bh, mt)) return;
+    int bh, item;
+    if (!map_item(p, bh, item)) return;
 
     const int tid = threadIdx.x;
     const int w = tid >> 6;
@@ -410,158 +464,168 @@ fa_fwd_32(Params p)
     const int g = lane >> 5;
 
     const int sq = p.sq, sk = p.sk;
-    const int q0 = mt * BM;
-    const float* __restrict__ Q = (const float*)p.q + (size_t)bh * sq * D;
-    const float* __restrict__ K = (const float*)p.k + (size_t)bh * sk * D;
-    const float* __restrict__ V = (const float*)p.v + (size_t)bh * sk * D;
-    float* __restrict__ O = (float*)p.o + (size_t)bh * sq * D;
+    auto process = [&](const int mt) {
+        const int q0 = mt * BM;
+        const float* __restrict__ Q = (const float*)p.q + (size_t)bh * sq * D;
+        const float* __restrict__ K = (const float*)p.k + (size_t)bh * sk * D;
+        const float* __restrict__ V = (const float*)p.v + (size_t)bh * sk * D;
+        float* __restrict__ O = (float*)p.o + (size_t)bh * sq * D;
 
-    const int qrow = q0 + w * 32 + l32;
-    const float qs = p.qsign ? -1.f : 1.f;
-    float qf[NKK];
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk)
-        qf[kk] = (qrow < sq) ? qs * Q[(size_t)qrow * D + kk * 2 + g] : 0.f;
+        const int qrow = q0 + w * 32 + l32;
+        const float qs = p.qsign ? -1.f : 1.f;
+        float qf[NKK];
+    #pragma unroll
+        for (int kk = 0; kk < NKK; ++kk)
+            qf[kk] = (qrow < sq) ? qs * Q[(size_t)qrow * D + kk * 2 + g] : 0.f;
 
-    const int q_end = min(q0 + BM, sq);
-    const int kv_end = CAUSAL ? min(q_end, sk) : sk;
-    const int nkv = (kv_end + BN - 1) / BN;
-    const int wq_first = q0 + w * 32;
-    const int wq_end = min(wq_first + 32, sq);
-    const int w_kv_end = (wq_end <= wq_first) ? 0 : (CAUSAL ? min(wq_end, sk) : sk);
-    const int w_nkv = (w_kv_end + BN - 1) / BN;
+        const int q_end = min(q0 + BM, sq);
+        const int kv_end = CAUSAL ? min(q_end, sk) : sk;
+        const int nkv = (kv_end + BN - 1) / BN;
+        const int wq_first = q0 + w * 32;
+        const int wq_end = min(wq_first + 32, sq);
+        const int w_kv_end = (wq_end <= wq_first) ? 0 : (CAUSAL ? min(wq_end, sk) : sk);
+        const int w_nkv = (w_kv_end + BN - 1) / BN;
 
-    float m_run = -INFINITY, l_run = 0.f;
-    f32x16_t oacc[NDT];
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
-
-    typedef float f32x4_t __attribute__((ext_vector_type(4)));
-    f32x4_t kreg[CH], vreg[CH];
-    auto load_tile = [&](int n0) {
-#pragma unroll
-        for (int i = 0; i < CH; ++i) {
-            const int c = tid + i * NT;
-            const int row = c / CPR, col = c % CPR;
-            const int key = n0 + row;
-            const bool ok = key < sk;
-            kreg[i] = ok ? *(const f32x4_t*)(K + (size_t)key * D + col * 4) : f32x4_t{0, 0, 0, 0};
-            vreg[i] = ok ? *(const f32x4_t*)(V + (size_t)key * D + col * 4) : f32x4_t{0, 0, 0, 0};
-        }
-    };
-    auto store_tile = [&](int buf) {
-        float* Ks = lds + buf * (KT + VT);
-        float* Vs = Ks + KT;
-#pragma unroll
-        for (int i = 0; i < CH; ++i) {
-            const int c = tid + i * NT;
-            const int row = c / CPR, col = c % CPR;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) Ks[row * KS + col * 4 + e] = kreg[i][e];
-            *(f32x4_t*)(Vs + row * VS + col * 4) = vreg[i];
-        }
-    };
-
-    const float c = p.c;
-
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
-
-    for (int t = 0; t < nkv; ++t) {
-        const int n0 = t * BN;
-        const bool more = (t + 1 < nkv);
-        if (more) load_tile(n0 + BN);
-
-        if (t < w_nkv) {
-            const float* Ks = lds + (t & 1) * (KT + VT);
-            const float* Vs = Ks + KT;
-
-            f32x16_t s[NKB];
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-#pragma unroll
-                for (int kk = 0; kk < NKK; ++kk) {
-                    const float a = Ks[(kb * 32 + l32) * KS + kk * 2 + g];
-                    s[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, qf[kk], s[kb], 0, 0, 0);
-                }
-            }
-
-            const bool need_mask = (n0 + BN > sk) || (CAUSAL && n0 + BN - 1 > wq_first);
-            if (need_mask) {
-#pragma unroll
-                for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = n0 + kb * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
-                        const bool dead = (key >= sk) || (CAUSAL && key > qrow);
-                        if (dead) s[kb][r] = -INFINITY;
-                    }
-            }
-
-            float mx = s[0][0];
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float m_new = fmaxf(m_run, mx * c);
-            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-            const float alpha = fast_exp2(m_run - m_use);
-            m_run = m_new;
-
-            float lsum = 0.f;
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float pr = fast_exp2(__builtin_fmaf(s[kb][r], c, -m_use));
-                    s[kb][r] = pr;
-                    lsum += pr;
-                }
-            l_run = l_run * alpha + lsum;
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
-
-            // O^T += V^T P^T, one key per lane half per step: register r of
-            // block kb holds key kb*32 + 8(r/4) + 4g + r%4
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = kb * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
-#pragma unroll
-                    for (int dt = 0; dt < NDT; ++dt) {
-                        const float a = Vs[key * VS + dt * 32 + l32];
-                        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, s[kb][r], oacc[dt], 0, 0, 0);
-                    }
-                }
-        }
-
-        if (more) store_tile((t + 1) & 1);
-        __syncthreads();
-    }
-
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
-    if (qrow < sq) {
-        const float inv = 1.f / l_tot;
-        float* orow = O + (size_t)qrow * D;
-#pragma unroll
+        float m_run = -INFINITY, l_run = 0.f;
+        f32x16_t oacc[NDT];
+    #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-            for (int rb = 0; rb < 4; ++rb) {
-                f32x4_t v4;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) v4[e] = oacc[dt][rb * 4 + e] * inv;
-                *(f32x4_t*)(orow + dt * 32 + rb * 8 + g * 4) = v4;
+    #pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
+
+        typedef float f32x4_t __attribute__((ext_vector_type(4)));
+        f32x4_t kreg[CH], vreg[CH];
+        auto load_tile = [&](int n0) {
+    #pragma unroll
+            for (int i = 0; i < CH; ++i) {
+                const int c = tid + i * NT;
+                const int row = c / CPR, col = c % CPR;
+                const int key = n0 + row;
+                const bool ok = key < sk;
+                kreg[i] = ok ? *(const f32x4_t*)(K + (size_t)key * D + col * 4) : f32x4_t{0, 0, 0, 0};
+                vreg[i] = ok ? *(const f32x4_t*)(V + (size_t)key * D + col * 4) : f32x4_t{0, 0, 0, 0};
             }
-        if (g == 0) p.lse[(size_t)bh * sq + qrow] = (m_run + __log2f(l_tot)) * kLn2;
+        };
+        auto store_tile = [&](int buf) {
+            float* Ks = lds + buf * (KT + VT);
+            float* Vs = Ks + KT;
+    #pragma unroll
+            for (int i = 0; i < CH; ++i) {
+                const int c = tid + i * NT;
+                const int row = c / CPR, col = c % CPR;
+    #pragma unroll
+                for (int e = 0; e < 4; ++e) Ks[row * KS + col * 4 + e] = kreg[i][e];
+                *(f32x4_t*)(Vs + row * VS + col * 4) = vreg[i];
+            }
+        };
+
+        const float c = p.c;
+
+        load_tile(0);
+        store_tile(0);
+        __syncthreads();
+
+        for (int t = 0; t < nkv; ++t) {
+            const int n0 = t * BN;
+            const bool more = (t + 1 < nkv);
+            if (more) load_tile(n0 + BN);
+
+            if (t < w_nkv) {
+                const float* Ks = lds + (t & 1) * (KT + VT);
+                const float* Vs = Ks + KT;
+
+                f32x16_t s[NKB];
+    #pragma unroll
+                for (int kb = 0; kb < NKB; ++kb) {
+    #pragma unroll
+                    for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+    #pragma unroll
+                    for (int kk = 0; kk < NKK; ++kk) {
+                        const float a = Ks[(kb * 32 + l32) * KS + kk * 2 + g];
+                        s[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, qf[kk], s[kb], 0, 0, 0);
+                    }
+                }
+
+                const bool need_mask = (n0 + BN > sk) || (CAUSAL && n0 + BN - 1 > wq_first);
+                if (need_mask) {
+    #pragma unroll
+                    for (int kb = 0; kb < NKB; ++kb)
+    #pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int key = n0 + kb * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
+                            const bool dead = (key >= sk) || (CAUSAL && key > qrow);
+                            if (dead) s[kb][r] = -INFINITY;
+                        }
+                }
+
+                float mx = s[0][0];
+    #pragma unroll
+                for (int kb = 0; kb < NKB; ++kb)
+    #pragma unroll
+                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+                mx = fmaxf(mx, __shfl_xor(mx, 32));
+                const float m_new = fmaxf(m_run, mx * c);
+                const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+                const float alpha = fast_exp2(m_run - m_use);
+                m_run = m_new;
+
+                float lsum = 0.f;
+    #pragma unroll
+                for (int kb = 0; kb < NKB; ++kb)
+    #pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const float pr = fast_exp2(__builtin_fmaf(s[kb][r], c, -m_use));
+                        s[kb][r] = pr;
+                        lsum += pr;
+                    }
+                l_run = l_run * alpha + lsum;
+    #pragma unroll
+                for (int dt = 0; dt < NDT; ++dt)
+    #pragma unroll
+                    for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+
+                // O^T += V^T P^T, one key per lane half per step: register r of
+                // block kb holds key kb*32 + 8(r/4) + 4g + r%4
+    #pragma unroll
+                for (int kb = 0; kb < NKB; ++kb)
+    #pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int key = kb * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
+    #pragma unroll
+                        for (int dt = 0; dt < NDT; ++dt) {
+                            const float a = Vs[key * VS + dt * 32 + l32];
+                            oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, s[kb][r], oacc[dt], 0, 0, 0);
+                        }
+                    }
+            }
+
+            if (more) store_tile((t + 1) & 1);
+            __syncthreads();
+        }
+
+        const float l_tot = l_run + __shfl_xor(l_run, 32);
+        if (qrow < sq) {
+            const float inv = 1.f / l_tot;
+            float* orow = O + (size_t)qrow * D;
+    #pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+    #pragma unroll
+                for (int rb = 0; rb < 4; ++rb) {
+                    f32x4_t v4;
+    #pragma unroll
+                    for (int e = 0; e < 4; ++e) v4[e] = oacc[dt][rb * 4 + e] * inv;
+                    *(f32x4_t*)(orow + dt * 32 + rb * 8 + g * 4) = v4;
+                }
+            if (g == 0) p.lse[(size_t)bh * sq + qrow] = (m_run + __log2f(l_tot)) * kLn2;
+        }
+    };
+
+    int mts[2];
+    const int nt = item_tiles(p, item, mts);
+    process(mts[0]);
+    if (nt > 1) {
+        __syncthreads();  // every wave is done with the LDS stages
+        process(mts[1]);
     }
 }
 

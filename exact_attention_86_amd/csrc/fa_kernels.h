@@ -19,9 +19,10 @@ struct Params {
     float c;         // |scale| * log2(e): exponent factor in log2 units
     uint32_t qsign;  // 0x80008000 (16-bit) or 1 (fp32) when scale < 0: Q enters negated
     int causal;      // 1: key j attends to query i iff j <= i
-    int n_mtiles;    // ceil(sq / block_m)
-    int n_tiles;     // bh * n_mtiles
-    int grid;        // workgroups launched
+    int n_mtiles;        // query tiles per head: ceil(sq / block_m)
+    int items_per_head;  // work items per head (causal: tile pairs)
+    int n_items;         // bh * items_per_head
+    int grid;            // workgroups launched
 };
 
 struct TileConfig {
