@@ -6,6 +6,7 @@
 One step is one fa_fwd call (the whole hot path: tile schedule, Q/K/V tile
 loads, S = QK^T, masking, online softmax, O += PV, epilogue) over the
 workload's synthetic inputs, which are resident in HBM before timing starts.
+Warm-up runs at least W steps and at least 0.5 s of launches (clocks settle).
 Prints ONE JSON line.  ``value`` is TFLOP/s with the usual attention count
 4*b*h*sq*sk*d (halved when causal) over the wall-clock of the K timed steps;
 ``roofline`` prices the kernel's average launch time (HIP events around each
@@ -95,8 +96,8 @@ def cpu_baseline(w: W.Workload, q, k, v, budget_s: float):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=W.HEADLINE.name, choices=sorted(W.BY_NAME))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
@@ -143,8 +144,15 @@ def main():
         if rc != fa.FA_OK:
             raise fa.FaError(rc, fa.fa_last_error())
 
-    for _ in range(args.warmup):
+    # untimed warm-up: at least W steps, and at least 0.5 s of launches so the
+    # GPU clocks have settled before the timed region
+    t_w = time.perf_counter()
+    n_w = 0
+    while n_w < args.warmup or time.perf_counter() - t_w < 0.5:
         step()
+        n_w += 1
+        if n_w % 8 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
 
     # per-launch kernel time: HIP events on the launch stream around each call

@@ -136,12 +136,13 @@ __device__ __forceinline__ uint32_t lds_addr(const void* ptr)
 // byte address lds_base + 16 i.  Issued as inline assembly so the compiler does
 // not serialise the other stage's LDS reads behind it; completion is awaited
 // explicitly with wait_copies() before the barrier that publishes the stage.
+template <int IMM>
 __device__ __forceinline__ void copy_1k(const void* sbase, uint32_t voff, uint32_t lds_base)
 {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+    asm volatile("s_add_u32 m0, %0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
                  :
-                 : "s"(lds_base), "v"(voff), "s"(sbase)
-                 : "memory", "m0");
+                 : "s"(lds_base), "v"(voff), "s"(sbase), "n"(IMM)
+                 : "memory", "m0", "scc");
 }
 
 __device__ __forceinline__ void wait_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
@@ -154,11 +155,25 @@ struct Stage {
     static constexpr int value = S;
 };
 
-template <int D, int BN, int NW, bool BF16, bool CAUSAL>
-__global__ void __launch_bounds__(NW * 64, 2)
+// f(Stage<0>{}), ..., f(Stage<N-1>{}): compile-time indices for immediates
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void static_for(F&& f)
+{
+    if constexpr (I < N) {
+        f(Stage<I>{});
+        static_for<N, I + 1>(f);
+    }
+}
+
+// QB 32-row query blocks per wave: every K or V operand read from LDS feeds
+// QB matrix-core instructions.  QB = 1 keeps two waves per SIMD; QB = 2 halves
+// the LDS traffic per MFMA at one wave per SIMD (more registers per wave).
+template <int D, int BN, int NW, int QB, bool BF16, bool CAUSAL>
+__global__ void __launch_bounds__(NW * 64, QB == 1 ? 2 : 1)
 fa_fwd_16(Params p)
 {
-    constexpr int BM = NW * 32;          // query rows per workgroup
+    constexpr int BM = NW * 32 * QB;     // query rows per workgroup tile
+    constexpr int WR = 32 * QB;          // query rows per wave
     constexpr int NKB = BN / 32;         // 32-key blocks per key tile
     constexpr int NDT = D / 32;          // 32-wide d tiles of the output
     constexpr int NKK = D / 16;          // k-steps of the score product
@@ -184,110 +199,120 @@ fa_fwd_16(Params p)
     const int lane = tid & 63;
     const int l32 = lane & 31;
     const int g = lane >> 5;
-
     const int sq = p.sq, sk = p.sk;
+    const float c = p.c;  // |scale| * log2(e)
+    constexpr float kRescaleThreshold = 8.f;  // lazy rescale: p <= 2^8
+    constexpr float kRescaleLimit = 256.f;    // partial row sum that forces the exact max
+
+    const uint16_t* __restrict__ Q = (const uint16_t*)p.q + (size_t)bh * sq * D;
+    const uint16_t* __restrict__ K = (const uint16_t*)p.k + (size_t)bh * sk * D;
+    const uint16_t* __restrict__ V = (const uint16_t*)p.v + (size_t)bh * sk * D;
+    uint16_t* __restrict__ O = (uint16_t*)p.o + (size_t)bh * sq * D;
+
+    // ---- global -> LDS copies.  Copy j of wave w fills LDS chunks
+    //      c = (w*DMA + j)*64 + lane: row c / CPR, physical chunk c % CPR,
+    //      fetched from the swizzled logical chunk.  Per-lane byte offsets
+    //      within a tile are fixed; the tile base is a scalar. ----
+    uint32_t dk[DMA], dv[DMA];
+#pragma unroll
+    for (int j = 0; j < DMA; ++j) {
+        const int cc = (w * DMA + j) * 64 + lane;
+        const int row = cc / CPR, pch = cc % CPR;
+        dk[j] = row * RB + ((pch ^ swz_k<CPR>(row)) << 4);
+        dv[j] = row * RB + ((pch ^ swz_v(row)) << 4);
+    }
+    const uint32_t lds0 = lds_addr(&lds[0][0][0]);
+    // copy j of K or V for the tile at n0 into stage `stage`.  full: the tile
+    // lies inside [0, sk) and the precomputed offsets apply; otherwise rows
+    // past the last key re-read the last key (finite data; those keys' scores
+    // are masked).
+    // LDS byte address of this wave's first copy slot (stage 0, K)
+    const uint32_t lbase = __builtin_amdgcn_readfirstlane(lds0 + w * DMA * 1024);
+    auto copy_k = [&](auto j_tag, auto st_tag, int n0, bool full) {
+        constexpr int J = decltype(j_tag)::value, ST = decltype(st_tag)::value;
+        const uint16_t* src = K + (size_t)n0 * D;
+        if (full) {
+            copy_1k<ST * 2 * TB + J * 1024>(src, dk[J], lbase);
+        } else {
+            const int cc = (w * DMA + J) * 64 + lane;
+            const int row = cc / CPR, pch = cc % CPR;
+            copy_1k<ST * 2 * TB + J * 1024>(src, min(row, sk - 1 - n0) * RB + ((pch ^ swz_k<CPR>(row)) << 4), lbase);
+        }
+    };
+    auto copy_v = [&](auto j_tag, auto st_tag, int n0, bool full) {
+        constexpr int J = decltype(j_tag)::value, ST = decltype(st_tag)::value;
+        const uint16_t* src = V + (size_t)n0 * D;
+        if (full) {
+            copy_1k<ST * 2 * TB + TB + J * 1024>(src, dv[J], lbase);
+        } else {
+            const int cc = (w * DMA + J) * 64 + lane;
+            const int row = cc / CPR, pch = cc % CPR;
+            copy_1k<ST * 2 * TB + TB + J * 1024>(src, min(row, sk - 1 - n0) * RB + ((pch ^ swz_v(row)) << 4), lbase);
+        }
+    };
+    auto issue_tile = [&](auto st_tag, int n0) {
+        const bool full = n0 + BN <= sk;
+        static_for<DMA>([&](auto j) {
+            copy_k(j, st_tag, n0, full);
+            copy_v(j, st_tag, n0, full);
+        });
+    };
+    // copies of the next tile are spread over the current tile's matrix-core
+    // work (K copies after each 32-key score block, V copies after each
+    // 16-key PV chunk) instead of one burst that stalls the wave at issue
+    constexpr int KC_PER = (DMA + NKB - 1) / NKB;
+    constexpr int VC_PER = (DMA + 2 * NKB - 1) / (2 * NKB);
+
+    // ---- per-lane LDS read offsets (bytes within a stage) ----
+    //  K (S^T A operand): row kb*32 + l32, logical chunk 2kk + g
+    uint32_t rk[NKR];
+#pragma unroll
+    for (int kk = 0; kk < NKR; ++kk) rk[kk] = l32 * RB + (((2 * kk + g) ^ swz_k<CPR>(l32)) << 4);
+    //  V (O^T A operand, transpose reads): lane 4r + c of its 16-lane group
+    //  reads key row 16kc + 8j + 4g + r, d = 32dt + 16*half + 4c
+    const int sub = lane & 15, vr = sub >> 2, vc = sub & 3, vhalf = (lane >> 4) & 1;
+    const int v_row = 4 * g + vr;
+    uint32_t rv[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+        rv[e] = TB + v_row * RB + (((e * 4 + 2 * vhalf + (vc >> 1)) ^ swz_v(v_row)) << 4) + (vc & 1) * 8;
+
     auto process = [&](const int mt) {
         const int q0 = mt * BM;
-        const uint16_t* __restrict__ Q = (const uint16_t*)p.q + (size_t)bh * sq * D;
-        const uint16_t* __restrict__ K = (const uint16_t*)p.k + (size_t)bh * sk * D;
-        const uint16_t* __restrict__ V = (const uint16_t*)p.v + (size_t)bh * sk * D;
-        uint16_t* __restrict__ O = (uint16_t*)p.o + (size_t)bh * sq * D;
 
         // ---- key range of this tile and of this wave ----
         const int q_end = min(q0 + BM, sq);
         const int kv_end = CAUSAL ? min(q_end, sk) : sk;
         const int nkv = (kv_end + BN - 1) / BN;
-        const int wq_first = q0 + w * 32;
-        const int wq_end = min(wq_first + 32, sq);
+        const int wq_first = q0 + w * WR;
+        const int wq_end = min(wq_first + WR, sq);
         const int w_kv_end = (wq_end <= wq_first) ? 0 : (CAUSAL ? min(wq_end, sk) : sk);
         const int w_nkv = (w_kv_end + BN - 1) / BN;
 
-        // ---- Q fragment: B operand of S^T = K Q^T, lane = query, 8 d values;
+        // ---- Q fragments: B operand of S^T = K Q^T, lane = query, 8 d values;
         //      rows past the end read the last row (finite, never stored) ----
-        const int qrow = q0 + w * 32 + l32;
-        const uint16_t* qptr = Q + (size_t)min(qrow, sq - 1) * D + g * 8;
-        u32x4_t qf[NKK];
-    #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) qf[kk] = *(const u32x4_t*)(qptr + kk * 16) ^ p.qsign;
-
-        // ---- global -> LDS copies.  Copy j of wave w fills LDS chunks
-        //      c = (w*DMA + j)*64 + lane: row c / CPR, physical chunk c % CPR,
-        //      fetched from the swizzled logical chunk.  Per-lane byte offsets
-        //      within a tile are fixed; the tile base is a scalar. ----
-        uint32_t dk[DMA], dv[DMA];
-    #pragma unroll
-        for (int j = 0; j < DMA; ++j) {
-            const int c = (w * DMA + j) * 64 + lane;
-            const int row = c / CPR, pch = c % CPR;
-            dk[j] = row * RB + ((pch ^ swz_k<CPR>(row)) << 4);
-            dv[j] = row * RB + ((pch ^ swz_v(row)) << 4);
+        int qrow[QB];
+        u32x4_t qf[QB][NKK];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            qrow[qb] = wq_first + qb * 32 + l32;
+            const uint16_t* qptr = Q + (size_t)min(qrow[qb], sq - 1) * D + g * 8;
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk) qf[qb][kk] = *(const u32x4_t*)(qptr + kk * 16) ^ p.qsign;
         }
-        const uint32_t lds0 = lds_addr(&lds[0][0][0]);
-        const uint32_t wofs = __builtin_amdgcn_readfirstlane(w * DMA * 1024);
-        // copy j of K or V for the tile at n0 into stage `stage`.  FULL: the tile
-        // lies inside [0, sk) and the precomputed offsets apply; otherwise rows
-        // past the last key re-read the last key (finite data; those keys' scores
-        // are masked).
-        auto copy_k = [&](int j, int n0, int stage, bool full) {
-            const uint16_t* src = K + (size_t)n0 * D;
-            const uint32_t l = lds0 + stage * 2 * TB + wofs + j * 1024;
-            if (full) {
-                copy_1k(src, dk[j], l);
-            } else {
-                const int c = (w * DMA + j) * 64 + lane;
-                const int row = c / CPR, pch = c % CPR;
-                copy_1k(src, min(row, sk - 1 - n0) * RB + ((pch ^ swz_k<CPR>(row)) << 4), l);
-            }
-        };
-        auto copy_v = [&](int j, int n0, int stage, bool full) {
-            const uint16_t* src = V + (size_t)n0 * D;
-            const uint32_t l = lds0 + stage * 2 * TB + TB + wofs + j * 1024;
-            if (full) {
-                copy_1k(src, dv[j], l);
-            } else {
-                const int c = (w * DMA + j) * 64 + lane;
-                const int row = c / CPR, pch = c % CPR;
-                copy_1k(src, min(row, sk - 1 - n0) * RB + ((pch ^ swz_v(row)) << 4), l);
-            }
-        };
-        auto issue_tile = [&](int n0, int stage) {
-            const bool full = n0 + BN <= sk;
-    #pragma unroll
-            for (int j = 0; j < DMA; ++j) {
-                copy_k(j, n0, stage, full);
-                copy_v(j, n0, stage, full);
-            }
-        };
-        // copies of the next tile are spread over the current tile's matrix-core
-        // work (K copies after each 32-key score block, V copies after each
-        // 16-key PV chunk) instead of one burst that stalls the wave at issue
-        constexpr int KC_PER = (DMA + NKB - 1) / NKB;
-        constexpr int VC_PER = (DMA + 2 * NKB - 1) / (2 * NKB);
 
-        // ---- per-lane LDS read offsets (bytes within a stage) ----
-        //  K (S^T A operand): row kb*32 + l32, logical chunk 2kk + g
-        uint32_t rk[NKR];
-    #pragma unroll
-        for (int kk = 0; kk < NKR; ++kk) rk[kk] = l32 * RB + (((2 * kk + g) ^ swz_k<CPR>(l32)) << 4);
-        //  V (O^T A operand, transpose reads): lane 4r + c of its 16-lane group
-        //  reads key row 16kc + 8j + 4g + r, d = 32dt + 16*half + 4c
-        const int sub = lane & 15, vr = sub >> 2, vc = sub & 3, vhalf = (lane >> 4) & 1;
-        const int v_row = 4 * g + vr;
-        uint32_t rv[2];
-    #pragma unroll
-        for (int e = 0; e < 2; ++e)
-            rv[e] = TB + v_row * RB + (((e * 4 + 2 * vhalf + (vc >> 1)) ^ swz_v(v_row)) << 4) + (vc & 1) * 8;
-
-        // ---- running softmax state (log2 units), output accumulator ----
-        float m_run = -INFINITY, l_run = 0.f;
-        f32x16_t oacc[NDT];
-    #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-    #pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
-
-        const float c = p.c;  // |scale| * log2(e)
-        constexpr float kRescaleThreshold = 8.f;  // lazy rescale: p <= 2^8
+        // ---- running softmax state (log2 units), output accumulators ----
+        float m_run[QB], l_run[QB];
+        f32x16_t oacc[QB][NDT];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            m_run[qb] = -INFINITY;
+            l_run[qb] = 0.f;
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[qb][dt][r] = 0.f;
+        }
 
         // PF_FULL: the next tile lies inside [0, sk) and its copies are issued
         // from inside this tile's math; otherwise the caller has issued them
@@ -297,92 +322,137 @@ fa_fwd_16(Params p)
             const char* sb = (const char*)&lds[S][0][0];
             const int nn = n0 + BN;  // prefetched tile
 
-            // ---- S^T = K Q^T on the matrix cores ----
-            f32x16_t s[NKB];
-    #pragma unroll
+            // ---- S^T = K Q^T on the matrix cores (each K read feeds QB) ----
+            f32x16_t s[QB][NKB];
+#pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
-    #pragma unroll
-                for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-    #pragma unroll
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) s[qb][kb][r] = 0.f;
+#pragma unroll
                 for (int kk = 0; kk < NKK; ++kk) {
                     const u32x4_t a = *(const u32x4_t*)(sb + rk[kk & 7] + kb * 32 * RB + (kk >> 3) * 256);
-                    s[kb] = mfma16(a, qf[kk], s[kb], BF16);
+#pragma unroll
+                    for (int qb = 0; qb < QB; ++qb) s[qb][kb] = mfma16(a, qf[qb][kk], s[qb][kb], BF16);
                 }
-    #pragma unroll
-                for (int j = kb * KC_PER; j < (kb + 1) * KC_PER && j < DMA; ++j)
-                    if (PF_FULL) copy_k(j, nn, S ^ 1, true);
+                if (PF_FULL)
+                    static_for<DMA>([&](auto j) {
+                        if (j.value >= kb * KC_PER && j.value < (kb + 1) * KC_PER)
+                            copy_k(j, Stage<S ^ 1>{}, nn, true);
+                    });
             }
 
             // ---- masks: ragged key tail, causal diagonal ----
             const bool need_mask = (n0 + BN > sk) || (CAUSAL && n0 + BN - 1 > wq_first);
             if (need_mask) {
-    #pragma unroll
-                for (int kb = 0; kb < NKB; ++kb)
-    #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = n0 + kb * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
-                        const bool dead = (key >= sk) || (CAUSAL && key > qrow);
-                        if (dead) s[kb][r] = -INFINITY;
-                    }
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+                    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int key = n0 + kb * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
+                            const bool dead = (key >= sk) || (CAUSAL && key > qrow[qb]);
+                            if (dead) s[qb][kb][r] = -INFINITY;
+                        }
             }
 
-            // ---- online softmax (log2 units) with lazy rescale ----
-            float mx = s[0][0];
-    #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
-    #pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-            mx = fmaxf(mx, __shfl_xor(mx, 32));  // lanes l and l+32 share a query
-            const float mt_ = mx * c;
-            // rescale only when some row's max grew by more than 2^8
-            if (__builtin_amdgcn_ballot_w64(mt_ > m_run + kRescaleThreshold)) {
-                const float m_new = fmaxf(m_run, mt_);
-                const float alpha = fast_exp2(m_run - m_new);  // 0 when m_run = -inf
-                l_run *= alpha;
-    #pragma unroll
-                for (int dt = 0; dt < NDT; ++dt)
-    #pragma unroll
-                    for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
-                m_run = m_new;
-            }
-            const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-
-            float lsum = 0.f;
-            uint32_t pk[NKB][8];
-    #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
-    #pragma unroll
-                for (int r = 0; r < 16; r += 2) {
-                    const float p0 = fast_exp2(__builtin_fmaf(s[kb][r], c, -m_use));
-                    const float p1 = fast_exp2(__builtin_fmaf(s[kb][r + 1], c, -m_use));
-                    lsum += p0 + p1;
-                    pk[kb][r >> 1] = pack2(p0, p1, BF16);
+            // ---- online softmax (log2 units) ----
+            // The running max m is only a reference point: any m gives the same
+            // result as long as no probability overflows.  So the tile is first
+            // exponentiated against the running max; only when that max is
+            // unset (a row's first tile) or some lane's partial row sum passes
+            // 2^8 (a probability may exceed 2^8) is the exact tile max taken,
+            // m raised (with O and l rescaled) if it grew by more than 2^8,
+            // and the tile exponentiated again.  Probabilities therefore stay
+            // <= 2^8 (fp16 P cannot overflow); the row sum adds the fp32 values.
+            u32x4_t pk[QB][2 * NKB];
+            float lsum[QB];
+            auto exponentiate = [&]() {
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) {
+                    const float m_use = (m_run[qb] == -INFINITY) ? 0.f : m_run[qb];
+                    float acc = 0.f;
+#pragma unroll
+                    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                        for (int r = 0; r < 16; r += 2) {
+                            const float p0 = fast_exp2(__builtin_fmaf(s[qb][kb][r], c, -m_use));
+                            const float p1 = fast_exp2(__builtin_fmaf(s[qb][kb][r + 1], c, -m_use));
+                            acc += p0 + p1;
+                            pk[qb][2 * kb + (r >> 3)][(r >> 1) & 3] = pack2(p0, p1, BF16);
+                        }
+                    lsum[qb] = acc;
                 }
-            l_run += lsum;
+            };
+            bool unset = false;
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) unset = unset || (m_run[qb] == -INFINITY);
+            bool exact = __builtin_amdgcn_ballot_w64(unset) != 0;
+            if (!exact) {
+                exponentiate();
+                bool big = false;
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) big = big || (lsum[qb] > kRescaleLimit);
+                exact = __builtin_amdgcn_ballot_w64(big) != 0;
+            }
+            if (exact) {
+                float mt_[QB];
+                bool grow = false;
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) {
+                    float mx = s[qb][0][0];
+#pragma unroll
+                    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qb][kb][r]);
+                    mx = fmaxf(mx, __shfl_xor(mx, 32));  // lanes l and l+32 share a query
+                    mt_[qb] = mx * c;
+                    grow = grow || (mt_[qb] > m_run[qb] + kRescaleThreshold);
+                }
+                if (__builtin_amdgcn_ballot_w64(grow)) {
+#pragma unroll
+                    for (int qb = 0; qb < QB; ++qb) {
+                        const float m_new = fmaxf(m_run[qb], mt_[qb]);
+                        const float alpha = fast_exp2(m_run[qb] - m_new);  // 0 when m_run = -inf
+                        l_run[qb] *= alpha;
+#pragma unroll
+                        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) oacc[qb][dt][r] *= alpha;
+                        m_run[qb] = m_new;
+                    }
+                }
+                exponentiate();
+            }
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) l_run[qb] += lsum[qb];
 
-            // ---- O^T += V^T P^T: A operand = two 4-key transpose reads ----
-    #pragma unroll
+            // ---- O^T += V^T P^T: A operand = two 4-key transpose reads, each
+            //      feeding QB matrix-core instructions ----
+#pragma unroll
             for (int kc = 0; kc < 2 * NKB; ++kc) {
-                const u32x4_t b = u32x4_t{pk[kc >> 1][(kc & 1) * 4 + 0], pk[kc >> 1][(kc & 1) * 4 + 1],
-                                          pk[kc >> 1][(kc & 1) * 4 + 2], pk[kc >> 1][(kc & 1) * 4 + 3]};
-    #pragma unroll
+#pragma unroll
                 for (int dt = 0; dt < NDT; ++dt) {
                     const char* va = sb + rv[dt & 1] + (dt >> 1) * 128 + kc * 16 * RB;
                     const v4i16_t x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(va));
                     const v4i16_t x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(va + 8 * RB));
                     const u32x4_t a = u32x4_t{__builtin_bit_cast(u32x2_t, x0)[0], __builtin_bit_cast(u32x2_t, x0)[1],
                                               __builtin_bit_cast(u32x2_t, x1)[0], __builtin_bit_cast(u32x2_t, x1)[1]};
-                    oacc[dt] = mfma16(a, b, oacc[dt], BF16);
+#pragma unroll
+                    for (int qb = 0; qb < QB; ++qb) oacc[qb][dt] = mfma16(a, pk[qb][kc], oacc[qb][dt], BF16);
                 }
-    #pragma unroll
-                for (int j = kc * VC_PER; j < (kc + 1) * VC_PER && j < DMA; ++j)
-                    if (PF_FULL) copy_v(j, nn, S ^ 1, true);
+                if (PF_FULL)
+                    static_for<DMA>([&](auto j) {
+                        if (j.value >= kc * VC_PER && j.value < (kc + 1) * VC_PER)
+                            copy_v(j, Stage<S ^ 1>{}, nn, true);
+                    });
             }
         };
 
-        // one key tile: publish its stage, prefetch the next tile into the other
-        // stage, then compute (stage index is a template constant so every LDS
-        // offset is an immediate)
+        // one key tile: publish its stage, then compute (the stage index is a
+        // template constant so every LDS offset is an immediate)
         auto step = [&](auto stage_tag, int t) {
             constexpr int S = decltype(stage_tag)::value;
             wait_copies();
@@ -392,12 +462,12 @@ fa_fwd_16(Params p)
             if (t < w_nkv && pf_full) {
                 compute(stage_tag, Stage<1>{}, t * BN);
             } else {
-                if (pf) issue_tile((t + 1) * BN, S ^ 1);
+                if (pf) issue_tile(Stage<S ^ 1>{}, (t + 1) * BN);
                 if (t < w_nkv) compute(stage_tag, Stage<0>{}, t * BN);
             }
         };
 
-        issue_tile(0, 0);
+        issue_tile(Stage<0>{}, 0);
         int t = 0;
         for (; t + 1 < nkv; t += 2) {
             step(Stage<0>{}, t);
@@ -406,19 +476,22 @@ fa_fwd_16(Params p)
         if (t < nkv) step(Stage<0>{}, t);
 
         // ---- epilogue: O = O^T / l, LSE = (m + log2 l) ln 2 ----
-        const float l_tot = l_run + __shfl_xor(l_run, 32);
-        if (qrow < sq) {
-            const float inv = 1.f / l_tot;
-            uint16_t* orow = O + (size_t)qrow * D;
-    #pragma unroll
-            for (int dt = 0; dt < NDT; ++dt)
-    #pragma unroll
-                for (int rb = 0; rb < 4; ++rb) {
-                    const uint32_t w0 = pack2(oacc[dt][rb * 4 + 0] * inv, oacc[dt][rb * 4 + 1] * inv, BF16);
-                    const uint32_t w1 = pack2(oacc[dt][rb * 4 + 2] * inv, oacc[dt][rb * 4 + 3] * inv, BF16);
-                    *(u32x2_t*)(orow + dt * 32 + rb * 8 + g * 4) = u32x2_t{w0, w1};
-                }
-            if (g == 0) p.lse[(size_t)bh * sq + qrow] = (m_run + __log2f(l_tot)) * kLn2;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            const float l_tot = l_run[qb] + __shfl_xor(l_run[qb], 32);
+            if (qrow[qb] < sq) {
+                const float inv = 1.f / l_tot;
+                uint16_t* orow = O + (size_t)qrow[qb] * D;
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                    for (int rb = 0; rb < 4; ++rb) {
+                        const uint32_t w0 = pack2(oacc[qb][dt][rb * 4 + 0] * inv, oacc[qb][dt][rb * 4 + 1] * inv, BF16);
+                        const uint32_t w1 = pack2(oacc[qb][dt][rb * 4 + 2] * inv, oacc[qb][dt][rb * 4 + 3] * inv, BF16);
+                        *(u32x2_t*)(orow + dt * 32 + rb * 8 + g * 4) = u32x2_t{w0, w1};
+                    }
+                if (g == 0) p.lse[(size_t)bh * sq + qrow[qb]] = (m_run[qb] + __log2f(l_tot)) * kLn2;
+            }
         }
     };
 
@@ -639,11 +712,11 @@ static hipError_t launch(KernelT kernel, int nw, const Params& p, hipStream_t st
     return hipGetLastError();
 }
 
-template <int D, int BN, int NW, bool BF16>
+template <int D, int BN, int NW, int QB, bool BF16>
 static hipError_t launch16(const Params& p, hipStream_t s)
 {
-    if (p.causal) return launch(fa_fwd_16<D, BN, NW, BF16, true>, NW, p, s);
-    return launch(fa_fwd_16<D, BN, NW, BF16, false>, NW, p, s);
+    if (p.causal) return launch(fa_fwd_16<D, BN, NW, QB, BF16, true>, NW, p, s);
+    return launch(fa_fwd_16<D, BN, NW, QB, BF16, false>, NW, p, s);
 }
 
 template <int D, int BN, int NW>
@@ -653,16 +726,17 @@ static hipError_t launch32(const Params& p, hipStream_t s)
     return launch(fa_fwd_32<D, BN, NW, false>, NW, p, s);
 }
 
-// tile configuration per (dtype, d): keep in step with the launch table below
+// tile configuration per (dtype, d): the launch table below dispatches on
+// exactly these values
 bool tile_config(int dtype, int d, TileConfig* tc)
 {
-    int bn = 0, nw = 0, lds = 0;
+    int bn = 0, nw = 0, qb = 1, lds = 0;
     if (dtype == 1 || dtype == 2) {
-        if (d == 64)       { bn = 128; nw = 4; }
-        else if (d == 128) { bn = 64; nw = 4; }
-        else if (d == 256) { bn = 32; nw = 4; }
+        if (d == 64)       { bn = 128; nw = 4; qb = 1; }
+        else if (d == 128) { bn = 64; nw = 4; qb = 1; }
+        else if (d == 256) { bn = 32; nw = 4; qb = 1; }
         else return false;
-        lds = 2 * (bn * (d + 8) + d * (bn + 8)) * 2;
+        lds = 4 * bn * d * 2;
     } else if (dtype == 0) {
         if (d == 64)       { bn = 32; nw = 2; }
         else if (d == 128) { bn = 32; nw = 2; }
@@ -671,25 +745,28 @@ bool tile_config(int dtype, int d, TileConfig* tc)
     } else {
         return false;
     }
-    tc->block_m = nw * 32;
+    tc->block_m = nw * 32 * qb;
     tc->block_n = bn;
     tc->waves = nw;
     tc->lds = lds;
+    tc->qb = qb;
     return true;
 }
 
 hipError_t launch_fwd(int dtype, int d, const Params& p, hipStream_t s)
 {
+    TileConfig tc;
+    if (!tile_config(dtype, d, &tc)) return hipErrorInvalidValue;
     switch (dtype) {
     case 2:
-        if (d == 64) return launch16<64, 128, 4, true>(p, s);
-        if (d == 128) return launch16<128, 64, 4, true>(p, s);
-        if (d == 256) return launch16<256, 32, 4, true>(p, s);
+        if (d == 64) return launch16<64, 128, 4, 1, true>(p, s);
+        if (d == 128) return launch16<128, 64, 4, 1, true>(p, s);
+        if (d == 256) return launch16<256, 32, 4, 1, true>(p, s);
         break;
     case 1:
-        if (d == 64) return launch16<64, 128, 4, false>(p, s);
-        if (d == 128) return launch16<128, 64, 4, false>(p, s);
-        if (d == 256) return launch16<256, 32, 4, false>(p, s);
+        if (d == 64) return launch16<64, 128, 4, 1, false>(p, s);
+        if (d == 128) return launch16<128, 64, 4, 1, false>(p, s);
+        if (d == 256) return launch16<256, 32, 4, 1, false>(p, s);
         break;
     case 0:
         if (d == 64) return launch32<64, 32, 2>(p, s);

@@ -27,6 +27,7 @@ struct Params {
 
 struct TileConfig {
     int block_m, block_n, waves, lds;
+    int qb;  // 32-row query blocks per wave
 };
 
 bool tile_config(int dtype, int d, TileConfig* tc);

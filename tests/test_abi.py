@@ -46,7 +46,7 @@ def test_version():
                                      (fa.FA_F32, 64), (fa.FA_F32, 128)])
 def test_query_config_served(dtype, d):
     cfg = fa.fa_query_config(dtype, d, 1)
-    assert cfg["block_m"] == 32 * cfg["waves"]
+    assert cfg["block_m"] % (32 * cfg["waves"]) == 0
     assert cfg["block_n"] % 32 == 0
     assert 0 < cfg["lds"] <= 160 * 1024
 
