@@ -53,7 +53,7 @@ def lib() -> ctypes.CDLL:
                              ctypes.c_float, ctypes.c_int, ctypes.c_int, vp]
         L.fa_fwd.restype = ctypes.c_int
         ip = ctypes.POINTER(ctypes.c_int)
-        L.fa_query_config.argtypes = [ctypes.c_int, i64, ctypes.c_int, ip, ip, ip, ip]
+        L.fa_query_config.argtypes = [ctypes.c_int, i64, ctypes.c_int, i64, i64, i64, i64, ip, ip, ip, ip]
         L.fa_query_config.restype = ctypes.c_int
         L.fa_last_error.argtypes = []
         L.fa_last_error.restype = ctypes.c_char_p
@@ -71,9 +71,12 @@ def fa_version() -> int:
     return lib().fa_version()
 
 
-def fa_query_config(dtype: int, d: int, causal: int = 0) -> dict:
+def fa_query_config(dtype: int, d: int, causal: int = 0, b: int = 1, h: int = 1, sq: int = 1,
+                    sk: int = 1) -> dict:
+    """Tiling of fa_fwd for a problem (the kernel choice may depend on sizes)."""
     vals = [ctypes.c_int(0) for _ in range(4)]
-    rc = lib().fa_query_config(int(dtype), int(d), int(causal), *[ctypes.byref(x) for x in vals])
+    rc = lib().fa_query_config(int(dtype), int(d), int(causal), int(b), int(h), int(sq), int(sk),
+                               *[ctypes.byref(x) for x in vals])
     if rc != FA_OK:
         raise FaError(rc, fa_last_error())
     return dict(zip(("block_m", "block_n", "waves", "lds"), (x.value for x in vals)))

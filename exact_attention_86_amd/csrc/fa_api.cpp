@@ -34,12 +34,14 @@ FA_API const char* fa_last_error(void) { return g_err; }
 
 FA_API int fa_version(void) { return 100; /* 0.1.0 */ }
 
-FA_API int fa_query_config(int dtype, int64_t d, int causal, int* block_m, int* block_n,
-                           int* waves, int* lds)
+FA_API int fa_query_config(int dtype, int64_t d, int causal, int64_t b, int64_t h, int64_t sq,
+                           int64_t sk, int* block_m, int* block_n, int* waves, int* lds)
 {
-    (void)causal;
+    (void)sk;
+    if (b <= 0 || h <= 0 || sq <= 0 || sk <= 0 || (causal != 0 && causal != 1))
+        return fail(FA_ERR_INVALID_ARG, "fa_query_config: sizes must be >= 1, causal 0 or 1");
     fa::TileConfig tc;
-    if (d <= 0 || d > 4096 || !fa::tile_config(dtype, (int)d, &tc))
+    if (d <= 0 || d > 4096 || !fa::tile_config(dtype, (int)d, b * h, sq, causal, &tc))
         return fail(FA_ERR_UNSUPPORTED, "fa_query_config: dtype/head size not served");
     if (block_m) *block_m = tc.block_m;
     if (block_n) *block_n = tc.block_n;
@@ -64,7 +66,7 @@ FA_API int fa_fwd(const void* q, const void* k, const void* v, void* o, float* l
     if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16)
         return fail(FA_ERR_UNSUPPORTED, "fa_fwd: unknown dtype");
     fa::TileConfig tc;
-    if (d > 4096 || !fa::tile_config(dtype, (int)d, &tc))
+    if (d > 4096 || !fa::tile_config(dtype, (int)d, b * h, sq, causal, &tc))
         return fail(FA_ERR_UNSUPPORTED, "fa_fwd: head size not served for this dtype");
     if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u)
         return fail(FA_ERR_MISALIGNED, "fa_fwd: q, k, v, o must be 16-byte aligned");
@@ -111,7 +113,7 @@ FA_API int fa_fwd(const void* q, const void* k, const void* v, void* o, float* l
     p.n_items = (int)n_items;
     p.grid = (int)(((n_items + 7) / 8) * 8);
 
-    hipError_t e = fa::launch_fwd(dtype, (int)d, p, (hipStream_t)stream);
+    hipError_t e = fa::launch_fwd(dtype, (int)d, tc, p, (hipStream_t)stream);
     if (e != hipSuccess) {
         snprintf(g_err, sizeof g_err, "fa_fwd: launch failed: %s", hipGetErrorString(e));
         return FA_ERR_HIP;

@@ -147,6 +147,18 @@ __device__ __forceinline__ void copy_1k(const void* sbase, uint32_t voff, uint32
 
 __device__ __forceinline__ void wait_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// s_waitcnt vmcnt(n) with expcnt/lgkmcnt left unconstrained (n < 16)
+template <int N>
+__device__ __forceinline__ void wait_copies_le()
+{
+    static_assert(N >= 0 && N < 16, "vmcnt immediate");
+    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+// workgroup barrier after this wave's LDS operations have completed; unlike
+// __syncthreads() it does not wait for outstanding global->LDS copies
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
 
@@ -505,6 +517,347 @@ fa_fwd_16(Params p)
 }
 
 // ---------------------------------------------------------------------------
+// 16-bit ping-pong kernel: two wave groups alternate matrix-core and softmax
+// ---------------------------------------------------------------------------
+// One workgroup of 8 waves per CU; waves 0-3 (group A) and 4-7 (group B) share
+// the SIMDs pairwise.  Time is cut into barrier-separated slots; in every slot
+// one group runs its matrix-core phase M(t) = { S(t) = K(t) Q^T,
+// O^T += V(t-1)^T P(t-1)^T } while the other runs its softmax phase
+// X(t) = softmax(S(t)) -> P(t), so the matrix cores always have a wave to feed.
+//   slot 2t:   A: M(t)   B: X(t-1)
+//   slot 2t+1: A: X(t)   B: M(t)
+// K(t) and V(t-1) are read in slots 2t and 2t+1; the copies of K(t+1) and V(t)
+// go out at the start of slot 2t into the stages freed after slot 2t-1 and are
+// awaited before the barrier that ends slot 2t+1.  Group A's wave i owns query
+// rows [64i, 64i+32) of the 256-row tile and group B's wave i rows
+// [64i+32, 64i+64), so both groups reach the causal diagonal together.
+template <int D, int BN, bool BF16, bool CAUSAL>
+__global__ void __launch_bounds__(512, 1)
+fa_fwd_16pp(Params p)
+{
+    constexpr int NW = 8;                // waves per workgroup
+    constexpr int BM = 256;              // query rows per workgroup tile
+    constexpr int NKB = BN / 32;         // 32-key blocks per key tile
+    constexpr int NDT = D / 32;          // 32-wide d tiles of the output
+    constexpr int NKK = D / 16;          // k-steps of the score product
+    constexpr int CPR = D / 8;           // 16-byte chunks per row
+    constexpr int RB = D * 2;            // bytes per K/V row
+    constexpr int TILE = BN * D;         // elements of one K or V tile
+    constexpr int TB = TILE * 2;         // bytes of one K or V tile
+    constexpr int NCH = BN * CPR;        // 16-byte chunks per tile
+    constexpr int DMA = NCH / 64 / NW;   // 1 KiB copies per wave per tensor per tile
+    constexpr int NKR = NKK < 8 ? NKK : 8;
+    static_assert(CPR >= 8, "swizzles need at least 8 chunks per row");
+    static_assert(DMA >= 1 && NCH % (64 * NW) == 0, "tile must split evenly over waves");
+    static_assert(4 * TB <= 160 * 1024, "LDS budget");
+
+    // [0..1] K stages, [2..3] V stages; BN rows x D, swizzled 16-byte chunks
+    __shared__ __attribute__((aligned(16))) uint16_t lds[4][TILE];
+
+    int bh, item;
+    if (!map_item(p, bh, item)) return;
+
+    const int tid = threadIdx.x;
+    const int w = tid >> 6;
+    const int grp = w >> 2;              // 0: group A, 1: group B
+    const int wi = w & 3;
+    const int lane = tid & 63;
+    const int l32 = lane & 31;
+    const int g = lane >> 5;
+    const int sq = p.sq, sk = p.sk;
+    const float c = p.c;  // |scale| * log2(e)
+    constexpr float kRescaleThreshold = 8.f;
+    constexpr float kRescaleLimit = 256.f;
+
+    const uint16_t* __restrict__ Q = (const uint16_t*)p.q + (size_t)bh * sq * D;
+    const uint16_t* __restrict__ K = (const uint16_t*)p.k + (size_t)bh * sk * D;
+    const uint16_t* __restrict__ V = (const uint16_t*)p.v + (size_t)bh * sk * D;
+    uint16_t* __restrict__ O = (uint16_t*)p.o + (size_t)bh * sq * D;
+
+    // ---- copies: wave w fills LDS chunks (w*DMA + j)*64 + lane of a tile ----
+    uint32_t dk[DMA], dv[DMA];
+#pragma unroll
+    for (int j = 0; j < DMA; ++j) {
+        const int cc = (w * DMA + j) * 64 + lane;
+        const int row = cc / CPR, pch = cc % CPR;
+        dk[j] = row * RB + ((pch ^ swz_k<CPR>(row)) << 4);
+        dv[j] = row * RB + ((pch ^ swz_v(row)) << 4);
+    }
+    const uint32_t lbase = __builtin_amdgcn_readfirstlane(lds_addr(&lds[0][0]) + w * DMA * 1024);
+    auto copy_k = [&](auto j_tag, auto st_tag, int n0, bool full) {
+        constexpr int J = decltype(j_tag)::value, ST = decltype(st_tag)::value;
+        const uint16_t* src = K + (size_t)n0 * D;
+        if (full) {
+            copy_1k<ST * TB + J * 1024>(src, dk[J], lbase);
+        } else {
+            const int cc = (w * DMA + J) * 64 + lane;
+            const int row = cc / CPR, pch = cc % CPR;
+            copy_1k<ST * TB + J * 1024>(src, min(row, sk - 1 - n0) * RB + ((pch ^ swz_k<CPR>(row)) << 4), lbase);
+        }
+    };
+    auto copy_v = [&](auto j_tag, auto st_tag, int n0, bool full) {
+        constexpr int J = decltype(j_tag)::value, ST = decltype(st_tag)::value;
+        const uint16_t* src = V + (size_t)n0 * D;
+        if (full) {
+            copy_1k<(2 + ST) * TB + J * 1024>(src, dv[J], lbase);
+        } else {
+            const int cc = (w * DMA + J) * 64 + lane;
+            const int row = cc / CPR, pch = cc % CPR;
+            copy_1k<(2 + ST) * TB + J * 1024>(src, min(row, sk - 1 - n0) * RB + ((pch ^ swz_v(row)) << 4), lbase);
+        }
+    };
+
+    // ---- per-lane LDS read offsets (bytes within a stage) ----
+    uint32_t rk[NKR];
+#pragma unroll
+    for (int kk = 0; kk < NKR; ++kk) rk[kk] = l32 * RB + (((2 * kk + g) ^ swz_k<CPR>(l32)) << 4);
+    const int sub = lane & 15, vr = sub >> 2, vc = sub & 3, vhalf = (lane >> 4) & 1;
+    const int v_row = 4 * g + vr;
+    uint32_t rv[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+        rv[e] = v_row * RB + (((e * 4 + 2 * vhalf + (vc >> 1)) ^ swz_v(v_row)) << 4) + (vc & 1) * 8;
+
+    auto process = [&](const int mt) {
+        const int q0 = mt * BM;
+        const int q_end = min(q0 + BM, sq);
+        const int kv_end = CAUSAL ? min(q_end, sk) : sk;
+        const int nkv = (kv_end + BN - 1) / BN;
+        const int wq_first = q0 + 64 * wi + 32 * grp;
+        const int wq_end = min(wq_first + 32, sq);
+        const int w_kv_end = (wq_end <= wq_first) ? 0 : (CAUSAL ? min(wq_end, sk) : sk);
+        const int w_nkv = (w_kv_end + BN - 1) / BN;
+        const int qrow = wq_first + l32;
+
+        // K(0) goes out before the Q loads
+        {
+            const bool f = BN <= sk;
+            static_for<DMA>([&](auto j) { copy_k(j, Stage<0>{}, 0, f); });
+        }
+        const uint16_t* qptr = Q + (size_t)min(qrow, sq - 1) * D + g * 8;
+        u32x4_t qf[NKK];
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) qf[kk] = *(const u32x4_t*)(qptr + kk * 16) ^ p.qsign;
+
+        float m_run = -INFINITY, l_run = 0.f;
+        f32x16_t oacc[NDT];
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
+        f32x16_t s[NKB];
+        u32x4_t pk[2 * NKB];
+
+        // ---- M(t): S(t) from K stage KS and PV(t-1) from V stage VS ----
+        auto mphase = [&](auto ks_tag, auto vs_tag, bool do_s, bool do_pv) {
+            constexpr int KS = decltype(ks_tag)::value, VS = decltype(vs_tag)::value;
+            const char* kb_ = (const char*)&lds[KS][0];
+            const char* vb_ = (const char*)&lds[2 + VS][0];
+            auto score = [&]() {
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+#pragma unroll
+                    for (int kk = 0; kk < NKK; ++kk) {
+                        const u32x4_t a = *(const u32x4_t*)(kb_ + rk[kk & 7] + kb * 32 * RB + (kk >> 3) * 256);
+                        s[kb] = mfma16(a, qf[kk], s[kb], BF16);
+                    }
+                }
+            };
+            auto pvm = [&]() {
+#pragma unroll
+                for (int kc = 0; kc < 2 * NKB; ++kc)
+#pragma unroll
+                    for (int dt = 0; dt < NDT; ++dt) {
+                        const char* va = vb_ + rv[dt & 1] + (dt >> 1) * 128 + kc * 16 * RB;
+                        const v4i16_t x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(va));
+                        const v4i16_t x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(va + 8 * RB));
+                        const u32x4_t a = u32x4_t{__builtin_bit_cast(u32x2_t, x0)[0], __builtin_bit_cast(u32x2_t, x0)[1],
+                                                  __builtin_bit_cast(u32x2_t, x1)[0], __builtin_bit_cast(u32x2_t, x1)[1]};
+                        oacc[dt] = mfma16(a, pk[kc], oacc[dt], BF16);
+                    }
+            };
+            if (do_s && do_pv) {
+                // 32 steps alternating a PV and an S matrix-core instruction;
+                // each step's LDS operand is fetched kAhead steps earlier into
+                // a small register ring so LDS latency hides behind the MFMAs
+                constexpr int NPV = 2 * NKB * NDT, NSC = NKB * NKK, NST = NPV + NSC;
+                static_assert(NPV == NSC, "alternating schedule needs equal halves");
+                constexpr int kAhead = 6;
+                u32x4_t ring[kAhead];
+                auto fetch = [&](auto i_tag) {
+                    constexpr int I = decltype(i_tag)::value;
+                    if constexpr (I % 2 == 0) {
+                        constexpr int op = I / 2, kc = op / NDT, dt = op % NDT;
+                        const char* va = vb_ + rv[dt & 1] + (dt >> 1) * 128 + kc * 16 * RB;
+                        const v4i16_t x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(va));
+                        const v4i16_t x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(va + 8 * RB));
+                        ring[I % kAhead] = u32x4_t{__builtin_bit_cast(u32x2_t, x0)[0], __builtin_bit_cast(u32x2_t, x0)[1],
+                                                   __builtin_bit_cast(u32x2_t, x1)[0], __builtin_bit_cast(u32x2_t, x1)[1]};
+                    } else {
+                        constexpr int op = I / 2, kb = op / NKK, kk = op % NKK;
+                        ring[I % kAhead] = *(const u32x4_t*)(kb_ + rk[kk & 7] + kb * 32 * RB + (kk >> 3) * 256);
+                    }
+                };
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+                static_for<kAhead>([&](auto i) { fetch(i); });
+                static_for<NST>([&](auto i_tag) {
+                    constexpr int I = decltype(i_tag)::value;
+                    const u32x4_t a = ring[I % kAhead];
+                    if constexpr (I + kAhead < NST) fetch(Stage<I + kAhead>{});
+                    if constexpr (I % 2 == 0) {
+                        constexpr int op = I / 2, kc = op / NDT, dt = op % NDT;
+                        oacc[dt] = mfma16(a, pk[kc], oacc[dt], BF16);
+                    } else {
+                        constexpr int op = I / 2, kb = op / NKK, kk = op % NKK;
+                        s[kb] = mfma16(a, qf[kk], s[kb], BF16);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                });
+            } else {
+                if (do_pv) pvm();
+                if (do_s) score();
+            }
+        };
+
+        // ---- X(t): online softmax of S(t) -> P(t) (log2 units); see fa_fwd_16
+        //      for the exponentiate-then-check scheme ----
+        auto xphase = [&](int n0) {
+            const bool need_mask = (n0 + BN > sk) || (CAUSAL && n0 + BN - 1 > wq_first);
+            if (need_mask) {
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int key = n0 + kb * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
+                        const bool dead = (key >= sk) || (CAUSAL && key > qrow);
+                        if (dead) s[kb][r] = -INFINITY;
+                    }
+            }
+            float lsum = 0.f;
+            auto exponentiate = [&]() {
+                const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+                float acc = 0.f;
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; r += 2) {
+                        const float p0 = fast_exp2(__builtin_fmaf(s[kb][r], c, -m_use));
+                        const float p1 = fast_exp2(__builtin_fmaf(s[kb][r + 1], c, -m_use));
+                        acc += p0 + p1;
+                        pk[2 * kb + (r >> 3)][(r >> 1) & 3] = pack2(p0, p1, BF16);
+                    }
+                lsum = acc;
+            };
+            bool exact = __builtin_amdgcn_ballot_w64(m_run == -INFINITY) != 0;
+            if (!exact) {
+                exponentiate();
+                exact = __builtin_amdgcn_ballot_w64(lsum > kRescaleLimit) != 0;
+            }
+            if (exact) {
+                float mx = s[0][0];
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+                mx = fmaxf(mx, __shfl_xor(mx, 32));  // lanes l and l+32 share a query
+                const float mt_ = mx * c;
+                if (__builtin_amdgcn_ballot_w64(mt_ > m_run + kRescaleThreshold)) {
+                    const float m_new = fmaxf(m_run, mt_);
+                    const float alpha = fast_exp2(m_run - m_new);  // 0 when m_run = -inf
+                    l_run *= alpha;
+#pragma unroll
+                    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+                    m_run = m_new;
+                }
+                exponentiate();
+            }
+            l_run += lsum;
+        };
+
+        // copies of K(t+1) -> K stage (t+1)&1 and V(t) -> V stage t&1
+        auto issue = [&](auto kst_tag, auto vst_tag, int t) {
+            if (t + 1 < nkv) {
+                const bool f = (t + 2) * BN <= sk;
+                static_for<DMA>([&](auto j) { copy_k(j, kst_tag, (t + 1) * BN, f); });
+            }
+            if (t < nkv) {
+                const bool f = (t + 1) * BN <= sk;
+                static_for<DMA>([&](auto j) { copy_v(j, vst_tag, t * BN, f); });
+            }
+        };
+
+        // M(t) for this wave, t = tile index; TP = t & 1
+        auto do_m = [&](auto tp_tag, int t) {
+            constexpr int TP = decltype(tp_tag)::value;
+            const bool ds = t < nkv && t < w_nkv;
+            const bool dp = t >= 1 && t - 1 < w_nkv;
+            mphase(Stage<TP>{}, Stage<TP ^ 1>{}, ds, dp);
+        };
+        auto do_x = [&](int t) {
+            if (t >= 0 && t < w_nkv) xphase(t * BN);
+        };
+
+        // prologue: K(0) resident for everyone
+        wait_copies();
+        __syncthreads();
+
+        // slots, unrolled by four (two tiles) so every stage index is a constant
+        const int nslots = 2 * nkv + 2;
+        for (int k = 0; k < nslots; k += 4) {
+            const int t = k >> 1;
+            // slot k = 2t (t even): A: M(t), B: X(t-1); copies K(t+1), V(t)
+            issue(Stage<1>{}, Stage<0>{}, t);
+            if (grp == 0) do_m(Stage<0>{}, t); else do_x(t - 1);
+            lds_barrier();
+            // slot 2t+1: A: X(t), B: M(t)
+            if (grp == 0) do_x(t); else do_m(Stage<0>{}, t);
+            wait_copies();
+            lds_barrier();
+            if (k + 2 >= nslots) break;
+            // slot 2t+2 = 2(t+1) (t+1 odd): A: M(t+1), B: X(t); copies K(t+2), V(t+1)
+            issue(Stage<0>{}, Stage<1>{}, t + 1);
+            if (grp == 0) do_m(Stage<1>{}, t + 1); else do_x(t);
+            lds_barrier();
+            // slot 2t+3: A: X(t+1), B: M(t+1)
+            if (grp == 0) do_x(t + 1); else do_m(Stage<1>{}, t + 1);
+            wait_copies();
+            lds_barrier();
+        }
+
+        // epilogue: O = O^T / l, LSE = (m + log2 l) ln 2
+        const float l_tot = l_run + __shfl_xor(l_run, 32);
+        if (qrow < sq) {
+            const float inv = 1.f / l_tot;
+            uint16_t* orow = O + (size_t)qrow * D;
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                for (int rb = 0; rb < 4; ++rb) {
+                    const uint32_t w0 = pack2(oacc[dt][rb * 4 + 0] * inv, oacc[dt][rb * 4 + 1] * inv, BF16);
+                    const uint32_t w1 = pack2(oacc[dt][rb * 4 + 2] * inv, oacc[dt][rb * 4 + 3] * inv, BF16);
+                    *(u32x2_t*)(orow + dt * 32 + rb * 8 + g * 4) = u32x2_t{w0, w1};
+                }
+            if (g == 0) p.lse[(size_t)bh * sq + qrow] = (m_run + __log2f(l_tot)) * kLn2;
+        }
+    };
+
+    int mts[2];
+    const int nt = item_tiles(p, item, mts);
+    process(mts[0]);
+    if (nt > 1) {
+        __syncthreads();  // every wave is done with the LDS stages
+        process(mts[1]);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // fp32 kernel (32x32x2 fp32 matrix cores; probabilities stay fp32)
 // ---------------------------------------------------------------------------
 template <int D, int BN, int NW, bool CAUSAL>
@@ -719,6 +1072,13 @@ static hipError_t launch16(const Params& p, hipStream_t s)
     return launch(fa_fwd_16<D, BN, NW, QB, BF16, false>, NW, p, s);
 }
 
+template <int D, int BN, bool BF16>
+static hipError_t launch16pp(const Params& p, hipStream_t s)
+{
+    if (p.causal) return launch(fa_fwd_16pp<D, BN, BF16, true>, 8, p, s);
+    return launch(fa_fwd_16pp<D, BN, BF16, false>, 8, p, s);
+}
+
 template <int D, int BN, int NW>
 static hipError_t launch32(const Params& p, hipStream_t s)
 {
@@ -726,16 +1086,27 @@ static hipError_t launch32(const Params& p, hipStream_t s)
     return launch(fa_fwd_32<D, BN, NW, false>, NW, p, s);
 }
 
-// tile configuration per (dtype, d): the launch table below dispatches on
-// exactly these values
-bool tile_config(int dtype, int d, TileConfig* tc)
+// tile configuration for a problem; the launch table below dispatches on
+// exactly these values.  fp16/bf16 with d = 128 uses the ping-pong kernel
+// (256-row tiles, one 8-wave workgroup per CU) when the problem has at least
+// one work item per CU, else the 4-wave kernel (128-row tiles, two per CU).
+bool tile_config(int dtype, int d, int64_t bh, int64_t sq, int causal, TileConfig* tc)
 {
-    int bn = 0, nw = 0, qb = 1, lds = 0;
+    constexpr int64_t kCUs = 256;
+    int bn = 0, nw = 0, qb = 1, lds = 0, kind = 0;
     if (dtype == 1 || dtype == 2) {
-        if (d == 64)       { bn = 128; nw = 4; qb = 1; }
-        else if (d == 128) { bn = 64; nw = 4; qb = 1; }
-        else if (d == 256) { bn = 32; nw = 4; qb = 1; }
-        else return false;
+        if (d == 64) {
+            bn = 128; nw = 4;
+        } else if (d == 128) {
+            const int64_t nq = (sq + 255) / 256;
+            const int64_t items = bh * (causal ? (nq + 1) / 2 : nq);
+            if (items >= kCUs) { bn = 64; nw = 8; kind = 1; }
+            else { bn = 64; nw = 4; }
+        } else if (d == 256) {
+            bn = 32; nw = 4;
+        } else {
+            return false;
+        }
         lds = 4 * bn * d * 2;
     } else if (dtype == 0) {
         if (d == 64)       { bn = 32; nw = 2; }
@@ -750,22 +1121,21 @@ bool tile_config(int dtype, int d, TileConfig* tc)
     tc->waves = nw;
     tc->lds = lds;
     tc->qb = qb;
+    tc->kind = kind;
     return true;
 }
 
-hipError_t launch_fwd(int dtype, int d, const Params& p, hipStream_t s)
+hipError_t launch_fwd(int dtype, int d, const TileConfig& tc, const Params& p, hipStream_t s)
 {
-    TileConfig tc;
-    if (!tile_config(dtype, d, &tc)) return hipErrorInvalidValue;
     switch (dtype) {
     case 2:
         if (d == 64) return launch16<64, 128, 4, 1, true>(p, s);
-        if (d == 128) return launch16<128, 64, 4, 1, true>(p, s);
+        if (d == 128) return tc.kind == 1 ? launch16pp<128, 64, true>(p, s) : launch16<128, 64, 4, 1, true>(p, s);
         if (d == 256) return launch16<256, 32, 4, 1, true>(p, s);
         break;
     case 1:
         if (d == 64) return launch16<64, 128, 4, 1, false>(p, s);
-        if (d == 128) return launch16<128, 64, 4, 1, false>(p, s);
+        if (d == 128) return tc.kind == 1 ? launch16pp<128, 64, false>(p, s) : launch16<128, 64, 4, 1, false>(p, s);
         if (d == 256) return launch16<256, 32, 4, 1, false>(p, s);
         break;
     case 0:

@@ -27,10 +27,11 @@ struct Params {
 
 struct TileConfig {
     int block_m, block_n, waves, lds;
-    int qb;  // 32-row query blocks per wave
+    int qb;    // 32-row query blocks per wave
+    int kind;  // 0: one wave group; 1: two ping-pong wave groups
 };
 
-bool tile_config(int dtype, int d, TileConfig* tc);
-hipError_t launch_fwd(int dtype, int d, const Params& p, hipStream_t stream);
+bool tile_config(int dtype, int d, int64_t bh, int64_t sq, int causal, TileConfig* tc);
+hipError_t launch_fwd(int dtype, int d, const TileConfig& tc, const Params& p, hipStream_t stream);
 
 }  // namespace fa

@@ -85,16 +85,18 @@ FA_API int fa_fwd(const void* q, const void* k, const void* v, void* o,
                   int64_t d, float scale, int causal, int dtype, void* stream);
 
 /*
- * fa_query_config -- the tiling fa_fwd uses for (dtype, d, causal).
+ * fa_query_config -- the tiling fa_fwd uses for a problem (dtype, d, causal,
+ * b, h, sq, sk); the choice of kernel may depend on the sizes.
  *   block_m  query rows per workgroup tile
  *   block_n  keys per inner step (one K/V tile through LDS)
  *   waves    wavefronts per workgroup (64 lanes each)
  *   lds      LDS bytes per workgroup
- * Any output pointer may be NULL.  Returns FA_OK or FA_ERR_UNSUPPORTED.
- * Host only; makes no HIP call.
+ * Any output pointer may be NULL.  Returns FA_OK, FA_ERR_INVALID_ARG (a size
+ * below 1, causal not 0/1) or FA_ERR_UNSUPPORTED.  Host only; no HIP call.
  */
-FA_API int fa_query_config(int dtype, int64_t d, int causal, int* block_m,
-                           int* block_n, int* waves, int* lds);
+FA_API int fa_query_config(int dtype, int64_t d, int causal, int64_t b, int64_t h,
+                           int64_t sq, int64_t sk, int* block_m, int* block_n,
+                           int* waves, int* lds);
 
 /* fa_last_error -- message of the last failing call on this host thread
  * ("" if none).  The pointer stays valid until the next call on the thread. */

@@ -51,6 +51,23 @@ def test_query_config_served(dtype, d):
     assert 0 < cfg["lds"] <= 160 * 1024
 
 
+def test_query_config_depends_on_size():
+    # d = 128 16-bit: 256-row ping-pong tiles when there is a work item per CU
+    big = fa.fa_query_config(fa.FA_BF16, 128, 1, 4, 32, 4096, 4096)
+    assert (big["block_m"], big["waves"]) == (256, 8)
+    small = fa.fa_query_config(fa.FA_F16, 128, 0, 2, 8, 1024, 1024)
+    assert (small["block_m"], small["waves"]) == (128, 4)
+
+
+def test_query_config_rejects_bad_sizes():
+    with pytest.raises(fa.FaError) as e:
+        fa.fa_query_config(fa.FA_BF16, 128, 0, 0, 1, 1, 1)
+    assert e.value.code == fa.FA_ERR_INVALID_ARG
+    with pytest.raises(fa.FaError) as e:
+        fa.fa_query_config(fa.FA_BF16, 128, 2, 1, 1, 1, 1)
+    assert e.value.code == fa.FA_ERR_INVALID_ARG
+
+
 @pytest.mark.parametrize("dtype,d", [(fa.FA_F32, 256), (fa.FA_BF16, 96), (fa.FA_BF16, 32),
                                      (3, 128), (-1, 128), (fa.FA_F16, 0)])
 def test_query_config_unsupported(dtype, d):

@@ -101,7 +101,7 @@ def test_workload_full_size_sampled_rows(idx, gpu):
     q, k, v = W.make(w)
     s = scale32(w.scale)
     o, lse = run_gpu(q, k, v, w.causal, s)
-    cfg = fa.fa_query_config(W.DTYPE_CODE[w.dtype], w.d, int(w.causal))
+    cfg = fa.fa_query_config(W.DTYPE_CODE[w.dtype], w.d, int(w.causal), w.b, w.h, w.sq, w.sk)
     rows = sample_rows(w, cfg["block_m"], seed=idx)
     ro, rl = oracle.attn_rows(q, k, v, rows, s, w.causal)
     go = o.reshape(-1, w.d)[torch.from_numpy(rows).cuda()].double().cpu().numpy()
@@ -145,6 +145,24 @@ SMALL = [
 def test_small_shapes_full_compare(case, gpu):
     dt, b, h, sq, sk, d, causal = case
     compare_full(W.shape("small", dt, b, h, sq, sk, d, causal, seed=sq * 7 + sk))
+
+
+# many heads with short sequences: enough work items for the 8-wave ping-pong
+# kernel (d = 128), compared over the whole output, ragged and causal
+PINGPONG = [
+    ("bf16", 1, 256, 300, 300, 128, True),
+    ("f16", 2, 128, 260, 260, 128, False),
+    ("bf16", 1, 256, 200, 333, 128, True),
+]
+
+
+@pytest.mark.parametrize("case", PINGPONG, ids=lambda c: "%s-b%dh%d-sq%d-sk%d-%s" % (
+    c[0], c[1], c[2], c[3], c[4], "causal" if c[6] else "full"))
+def test_pingpong_shapes_full_compare(case, gpu):
+    dt, b, h, sq, sk, d, causal = case
+    cfg = fa.fa_query_config(W.DTYPE_CODE[dt], d, int(causal), b, h, sq, sk)
+    assert cfg["waves"] == 8
+    compare_full(W.shape("pp", dt, b, h, sq, sk, d, causal, seed=sq + sk))
 
 
 @pytest.mark.parametrize("scale", [-0.125, 0.0, 0.5])
