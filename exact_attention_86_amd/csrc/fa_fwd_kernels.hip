@@ -520,15 +520,18 @@ fa_fwd_16(Params p)
 // 16-bit ping-pong kernel: two wave groups alternate matrix-core and softmax
 // ---------------------------------------------------------------------------
 // One workgroup of 8 waves per CU; waves 0-3 (group A) and 4-7 (group B) share
-// the SIMDs pairwise.  Time is cut into barrier-separated slots; in every slot
-// one group runs its matrix-core phase M(t) = { S(t) = K(t) Q^T,
-// O^T += V(t-1)^T P(t-1)^T } while the other runs its softmax phase
-// X(t) = softmax(S(t)) -> P(t), so the matrix cores always have a wave to feed.
+// the SIMDs pairwise.  Each key tile t is a window of two slots that starts at a
+// workgroup barrier; group A runs its matrix-core phase M(t) = { S(t) = K(t) Q^T,
+// O^T += V(t-1)^T P(t-1)^T } and then its softmax phase X(t) = softmax(S(t)) ->
+// P(t), group B runs X(t-1) and then M(t):
 //   slot 2t:   A: M(t)   B: X(t-1)
 //   slot 2t+1: A: X(t)   B: M(t)
-// K(t) and V(t-1) are read in slots 2t and 2t+1; the copies of K(t+1) and V(t)
-// go out at the start of slot 2t into the stages freed after slot 2t-1 and are
-// awaited before the barrier that ends slot 2t+1.  Group A's wave i owns query
+// so each SIMD has one wave issuing matrix-core work while the other issues
+// VALU work.  The slots need no barrier between them (no LDS stage changes
+// hands inside a window), so a wave moves on as soon as its own phase ends.
+// K(t) and V(t-1) are read inside window t; the copies of K(t+1) and V(t) go
+// out at its start into the stages freed by window t-1 and are awaited before
+// the barrier that ends it.  Group A's wave i owns query
 // rows [64i, 64i+32) of the 256-row tile and group B's wave i rows
 // [64i+32, 64i+64), so both groups reach the causal diagonal together.
 template <int D, int BN, bool BF16, bool CAUSAL>
@@ -815,7 +818,6 @@ fa_fwd_16pp(Params p)
             // slot k = 2t (t even): A: M(t), B: X(t-1); copies K(t+1), V(t)
             issue(Stage<1>{}, Stage<0>{}, t);
             if (grp == 0) do_m(Stage<0>{}, t); else do_x(t - 1);
-            lds_barrier();
             // slot 2t+1: A: X(t), B: M(t)
             if (grp == 0) do_x(t); else do_m(Stage<0>{}, t);
             wait_copies();
@@ -824,7 +826,6 @@ fa_fwd_16pp(Params p)
             // slot 2t+2 = 2(t+1) (t+1 odd): A: M(t+1), B: X(t); copies K(t+2), V(t+1)
             issue(Stage<0>{}, Stage<1>{}, t + 1);
             if (grp == 0) do_m(Stage<1>{}, t + 1); else do_x(t);
-            lds_barrier();
             // slot 2t+3: A: X(t+1), B: M(t+1)
             if (grp == 0) do_x(t + 1); else do_m(Stage<1>{}, t + 1);
             wait_copies();
