@@ -1,11 +1,13 @@
 """Throughput of the exact-attention prefill forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--no-cpu-baseline]
+                    [--split N] [--no-cpu-baseline]
 
 One step is one fa_fwd call (the whole hot path: tile schedule, Q/K/V tile
 loads, S = QK^T, masking, online softmax, O += PV, epilogue) over the
 workload's synthetic inputs, which are resident in HBM before timing starts.
+With --split N > 1 a step is one fa_fwd_split call (split-KV forward plus the
+merge kernel; the workspace is allocated before timing).
 Warm-up runs at least W steps and at least 0.5 s of launches (clocks settle).
 Prints ONE JSON line.  ``value`` is TFLOP/s with the usual attention count
 4*b*h*sq*sk*d (halved when causal) over the wall-clock of the K timed steps;
@@ -99,6 +101,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=W.HEADLINE.name, choices=sorted(W.BY_NAME))
+    ap.add_argument("--split", type=int, default=1, metavar="N",
+                    help="split-KV parts per query tile (fa_fwd_split); 1 = fa_fwd")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -138,11 +142,21 @@ def main():
     code = W.DTYPE_CODE[w.dtype]
     ptrs = (qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), od.data_ptr(), lsed.data_ptr())
 
-    def step():
-        rc = fa.fa_fwd(*ptrs, w.b, w.h, w.sq, w.sk, w.d, scale, int(w.causal), code,
-                       stream.cuda_stream)
-        if rc != fa.FA_OK:
-            raise fa.FaError(rc, fa.fa_last_error())
+    if args.split > 1:
+        ws_bytes = fa.fa_split_workspace_bytes(w.b, w.h, w.sq, w.d, args.split)
+        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+
+        def step():
+            rc = fa.fa_fwd_split(*ptrs, w.b, w.h, w.sq, w.sk, w.d, scale, int(w.causal), code,
+                                 args.split, ws.data_ptr(), ws_bytes, stream.cuda_stream)
+            if rc != fa.FA_OK:
+                raise fa.FaError(rc, fa.fa_last_error())
+    else:
+        def step():
+            rc = fa.fa_fwd(*ptrs, w.b, w.h, w.sq, w.sk, w.d, scale, int(w.causal), code,
+                           stream.cuda_stream)
+            if rc != fa.FA_OK:
+                raise fa.FaError(rc, fa.fa_last_error())
 
     # untimed warm-up: at least W steps, and at least 0.5 s of launches so the
     # GPU clocks have settled before the timed region
@@ -190,10 +204,11 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic",
-        "config": dict(w.describe(), kernel="fa_fwd", parallelism="none (one GPU)"),
+        "config": dict(w.describe(), kernel="fa_fwd" if args.split == 1 else "fa_fwd_split",
+                       nsplit=args.split, parallelism="none (one GPU)"),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": traffic_record(w)},
+                     "traffic": traffic_record(w) if args.split == 1 else None},
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on a sample (~%.0f s)" % args.cpu_budget)

@@ -8,7 +8,11 @@ raise.
 
     fa_fwd(q, k, v, o, lse, b, h, sq, sk, d, scale, causal, dtype, stream)
         the C entry point with raw device addresses (ints) and sizes
-    attention(q, k, v, causal=False, scale=None, out=None, lse=None)
+    fa_fwd_split(q, k, v, o, lse, b, h, sq, sk, d, scale, causal, dtype, nsplit,
+                 workspace, workspace_bytes, stream)
+        split-KV forward; fa_split_workspace_bytes(b, h, sq, d, nsplit) sizes
+        its workspace
+    attention(q, k, v, causal=False, scale=None, out=None, lse=None, nsplit=1)
         convenience wrapper over torch device tensors [b, h, s, d]
 """
 from __future__ import annotations
@@ -59,6 +63,12 @@ def lib() -> ctypes.CDLL:
         L.fa_last_error.restype = ctypes.c_char_p
         L.fa_version.argtypes = []
         L.fa_version.restype = ctypes.c_int
+        L.fa_fwd_split.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                                   ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                   vp, ctypes.c_size_t, vp]
+        L.fa_fwd_split.restype = ctypes.c_int
+        L.fa_split_workspace_bytes.argtypes = [i64, i64, i64, i64, ctypes.c_int]
+        L.fa_split_workspace_bytes.restype = ctypes.c_size_t
         _lib = L
         return L
 
@@ -88,6 +98,19 @@ def fa_fwd(q, k, v, o, lse, b, h, sq, sk, d, scale, causal, dtype, stream) -> in
                         float(scale), int(causal), int(dtype), stream)
 
 
+def fa_fwd_split(q, k, v, o, lse, b, h, sq, sk, d, scale, causal, dtype, nsplit, workspace,
+                 workspace_bytes, stream) -> int:
+    """The split-KV C entry point: device addresses as ints, returns the status code."""
+    return lib().fa_fwd_split(q, k, v, o, lse, int(b), int(h), int(sq), int(sk), int(d),
+                              float(scale), int(causal), int(dtype), int(nsplit), workspace,
+                              int(workspace_bytes), stream)
+
+
+def fa_split_workspace_bytes(b, h, sq, d, nsplit) -> int:
+    """Workspace bytes fa_fwd_split needs (0 for nsplit = 1 or invalid sizes)."""
+    return int(lib().fa_split_workspace_bytes(int(b), int(h), int(sq), int(d), int(nsplit)))
+
+
 def _dtype_code(t) -> int:
     import torch
     codes = {torch.float32: FA_F32, torch.float16: FA_F16, torch.bfloat16: FA_BF16}
@@ -97,12 +120,13 @@ def _dtype_code(t) -> int:
 
 
 def attention(q, k, v, causal: bool = False, scale: float | None = None, out=None,
-              lse=None, stream=None):
+              lse=None, stream=None, nsplit: int = 1, workspace=None):
     """O, LSE for torch device tensors q [b,h,sq,d], k/v [b,h,sk,d].
 
     Outputs are allocated with torch when not given.  Runs on ``stream`` (a
     torch stream) or torch's current stream; returns (O, LSE) without
-    synchronising.
+    synchronising.  ``nsplit`` > 1 runs the split-KV forward; its workspace
+    (a torch uint8 device tensor) is allocated when not given.
     """
     import torch
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
@@ -124,8 +148,17 @@ def attention(q, k, v, causal: bool = False, scale: float | None = None, out=Non
     if lse is None:
         lse = torch.empty((b, h, sq), dtype=torch.float32, device=q.device)
     s = stream if stream is not None else torch.cuda.current_stream(q.device)
-    rc = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                b, h, sq, sk, d, scale, int(bool(causal)), _dtype_code(q), s.cuda_stream)
+    if nsplit == 1:
+        rc = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                    b, h, sq, sk, d, scale, int(bool(causal)), _dtype_code(q), s.cuda_stream)
+    else:
+        need = fa_split_workspace_bytes(b, h, sq, d, nsplit)
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        nbytes = workspace.numel() * workspace.element_size()
+        rc = fa_fwd_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                          b, h, sq, sk, d, scale, int(bool(causal)), _dtype_code(q), nsplit,
+                          workspace.data_ptr(), nbytes, s.cuda_stream)
     if rc != FA_OK:
         raise FaError(rc, fa_last_error())
     return out, lse

@@ -51,63 +51,80 @@ FA_API int fa_query_config(int dtype, int64_t d, int causal, int64_t b, int64_t 
     return FA_OK;
 }
 
-FA_API int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-                  int64_t b, int64_t h, int64_t sq, int64_t sk, int64_t d, float scale,
-                  int causal, int dtype, void* stream)
+// checks shared by fa_fwd and fa_fwd_split; fills the launch parameters
+// except the schedule fields.  `who` prefixes the messages.
+static int check_common(const char* who, const void* q, const void* k, const void* v, void* o, float* lse,
+                        int64_t b, int64_t h, int64_t sq, int64_t sk, int64_t d, float scale, int causal,
+                        int dtype, fa::Params* p)
 {
-    if (!q || !k || !v || !o || !lse)
-        return fail(FA_ERR_INVALID_ARG, "fa_fwd: NULL pointer");
+    char msg[160];
+    auto bad = [&](int code, const char* what) {
+        snprintf(msg, sizeof msg, "%s: %s", who, what);
+        return fail(code, msg);
+    };
+    if (!q || !k || !v || !o || !lse) return bad(FA_ERR_INVALID_ARG, "NULL pointer");
     if (b <= 0 || h <= 0 || sq <= 0 || sk <= 0 || d <= 0)
-        return fail(FA_ERR_INVALID_ARG, "fa_fwd: b, h, sq, sk and d must be >= 1");
-    if (!isfinite(scale))
-        return fail(FA_ERR_INVALID_ARG, "fa_fwd: scale must be finite");
-    if (causal != 0 && causal != 1)
-        return fail(FA_ERR_INVALID_ARG, "fa_fwd: causal must be 0 or 1");
-    if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16)
-        return fail(FA_ERR_UNSUPPORTED, "fa_fwd: unknown dtype");
-    fa::TileConfig tc;
-    if (d > 4096 || !fa::tile_config(dtype, (int)d, b * h, sq, causal, &tc))
-        return fail(FA_ERR_UNSUPPORTED, "fa_fwd: head size not served for this dtype");
+        return bad(FA_ERR_INVALID_ARG, "b, h, sq, sk and d must be >= 1");
+    if (!isfinite(scale)) return bad(FA_ERR_INVALID_ARG, "scale must be finite");
+    if (causal != 0 && causal != 1) return bad(FA_ERR_INVALID_ARG, "causal must be 0 or 1");
+    if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return bad(FA_ERR_UNSUPPORTED, "unknown dtype");
+    if (d > 4096) return bad(FA_ERR_UNSUPPORTED, "head size not served for this dtype");
     if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u)
-        return fail(FA_ERR_MISALIGNED, "fa_fwd: q, k, v, o must be 16-byte aligned");
-    if ((uintptr_t)lse & 3u)
-        return fail(FA_ERR_MISALIGNED, "fa_fwd: lse must be 4-byte aligned");
-
+        return bad(FA_ERR_MISALIGNED, "q, k, v, o must be 16-byte aligned");
+    if ((uintptr_t)lse & 3u) return bad(FA_ERR_MISALIGNED, "lse must be 4-byte aligned");
     // per-head slices use 32-bit offsets; head counts and the grid are int32
     const int64_t lim = INT32_MAX;
     if (sq * d > lim || sk * d > lim || b * h > lim || b > lim || h > lim)
-        return fail(FA_ERR_TOO_LARGE, "fa_fwd: a per-head slice exceeds 2^31-1 elements");
-    // causal work items pair query tile nQ-1-i with tile i (equal cost)
-    const int64_t n_mtiles = (sq + tc.block_m - 1) / tc.block_m;
-    const int64_t items_per_head = causal ? (n_mtiles + 1) / 2 : n_mtiles;
-    const int64_t n_items = b * h * items_per_head;
-    if (n_items > lim - 8)
-        return fail(FA_ERR_TOO_LARGE, "fa_fwd: too many tiles for one launch");
-
+        return bad(FA_ERR_TOO_LARGE, "a per-head slice exceeds 2^31-1 elements");
     const size_t esz = dtype == FA_F32 ? 4 : 2;
     const size_t nq = (size_t)(b * h * sq * d) * esz, nk = (size_t)(b * h * sk * d) * esz;
     const size_t nl = (size_t)(b * h * sq) * 4;
     if (overlap(o, nq, q, nq) || overlap(o, nq, k, nk) || overlap(o, nq, v, nk) ||
         overlap(lse, nl, q, nq) || overlap(lse, nl, k, nk) || overlap(lse, nl, v, nk) ||
         overlap(lse, nl, o, nq))
-        return fail(FA_ERR_INVALID_ARG, "fa_fwd: o and lse must not overlap the inputs or each other");
+        return bad(FA_ERR_INVALID_ARG, "o and lse must not overlap the inputs or each other");
 
-    fa::Params p;
-    p.q = q;
-    p.k = k;
-    p.v = v;
-    p.o = o;
-    p.lse = lse;
-    p.bh = (int)(b * h);
-    p.sq = (int)sq;
-    p.sk = (int)sk;
+    p->q = q;
+    p->k = k;
+    p->v = v;
+    p->o = o;
+    p->lse = lse;
+    p->bh = (int)(b * h);
+    p->sq = (int)sq;
+    p->sk = (int)sk;
     // exponent factor in log2 units; a zero scale keeps a tiny positive factor
     // so masked (-inf) scores still map to exp2(-inf) = 0 and every live score
     // gives exp2(0 +- 1e-30 |s|) = 1 exactly in fp32
     const float a = fabsf(scale);
-    p.c = a > 0.f ? (float)((double)a * 1.4426950408889634) : 1e-30f;
-    p.qsign = scale < 0.f ? (dtype == FA_F32 ? 1u : 0x80008000u) : 0u;
-    p.causal = causal;
+    p->c = a > 0.f ? (float)((double)a * 1.4426950408889634) : 1e-30f;
+    p->qsign = scale < 0.f ? (dtype == FA_F32 ? 1u : 0x80008000u) : 0u;
+    p->causal = causal;
+    p->nsplit = 1;
+    p->ws = nullptr;
+    return FA_OK;
+}
+
+static size_t split_ws_bytes(int64_t b, int64_t h, int64_t sq, int64_t d, int64_t nsplit)
+{
+    return (size_t)nsplit * (size_t)(b * h * sq) * (size_t)(d + 1) * 4;
+}
+
+FA_API int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                  int64_t b, int64_t h, int64_t sq, int64_t sk, int64_t d, float scale,
+                  int causal, int dtype, void* stream)
+{
+    fa::Params p;
+    const int rc = check_common("fa_fwd", q, k, v, o, lse, b, h, sq, sk, d, scale, causal, dtype, &p);
+    if (rc != FA_OK) return rc;
+    fa::TileConfig tc;
+    if (!fa::tile_config(dtype, (int)d, b * h, sq, causal, &tc))
+        return fail(FA_ERR_UNSUPPORTED, "fa_fwd: head size not served for this dtype");
+    // causal work items pair query tile nQ-1-i with tile i (equal cost)
+    const int64_t n_mtiles = (sq + tc.block_m - 1) / tc.block_m;
+    const int64_t items_per_head = causal ? (n_mtiles + 1) / 2 : n_mtiles;
+    const int64_t n_items = b * h * items_per_head;
+    if (n_items > INT32_MAX - 8)
+        return fail(FA_ERR_TOO_LARGE, "fa_fwd: too many tiles for one launch");
     p.n_mtiles = (int)n_mtiles;
     p.items_per_head = (int)items_per_head;
     p.n_items = (int)n_items;
@@ -116,6 +133,60 @@ FA_API int fa_fwd(const void* q, const void* k, const void* v, void* o, float* l
     hipError_t e = fa::launch_fwd(dtype, (int)d, tc, p, (hipStream_t)stream);
     if (e != hipSuccess) {
         snprintf(g_err, sizeof g_err, "fa_fwd: launch failed: %s", hipGetErrorString(e));
+        return FA_ERR_HIP;
+    }
+    g_err[0] = 0;
+    return FA_OK;
+}
+
+FA_API size_t fa_split_workspace_bytes(int64_t b, int64_t h, int64_t sq, int64_t d, int nsplit)
+{
+    if (b <= 0 || h <= 0 || sq <= 0 || d <= 0 || nsplit < 1 || nsplit > FA_MAX_SPLIT) return 0;
+    if (nsplit == 1) return 0;
+    return split_ws_bytes(b, h, sq, d, nsplit);
+}
+
+FA_API int fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int64_t b, int64_t h, int64_t sq, int64_t sk, int64_t d, float scale,
+                        int causal, int dtype, int nsplit, void* workspace, size_t workspace_bytes,
+                        void* stream)
+{
+    if (nsplit < 1 || nsplit > FA_MAX_SPLIT)
+        return fail(FA_ERR_INVALID_ARG, "fa_fwd_split: nsplit must be in [1, 64]");
+    if (nsplit == 1)  // one part: exactly fa_fwd; the workspace is not touched
+        return fa_fwd(q, k, v, o, lse, b, h, sq, sk, d, scale, causal, dtype, stream);
+    fa::Params p;
+    const int rc = check_common("fa_fwd_split", q, k, v, o, lse, b, h, sq, sk, d, scale, causal, dtype, &p);
+    if (rc != FA_OK) return rc;
+    fa::TileConfig tc;
+    if (!fa::tile_config_split(dtype, (int)d, &tc))
+        return fail(FA_ERR_UNSUPPORTED, "fa_fwd_split: fp16/bf16 with d = 64, 128 or 256 only");
+    if (!workspace) return fail(FA_ERR_INVALID_ARG, "fa_fwd_split: NULL workspace");
+    if ((uintptr_t)workspace & 15u) return fail(FA_ERR_MISALIGNED, "fa_fwd_split: workspace must be 16-byte aligned");
+    const size_t need = split_ws_bytes(b, h, sq, d, nsplit);
+    if (workspace_bytes < need)
+        return fail(FA_ERR_INVALID_ARG, "fa_fwd_split: workspace smaller than fa_split_workspace_bytes()");
+    const size_t nq = (size_t)(b * h * sq * d) * 2, nk = (size_t)(b * h * sk * d) * 2;
+    const size_t nl = (size_t)(b * h * sq) * 4;
+    if (overlap(workspace, need, q, nq) || overlap(workspace, need, k, nk) || overlap(workspace, need, v, nk) ||
+        overlap(workspace, need, o, nq) || overlap(workspace, need, lse, nl))
+        return fail(FA_ERR_INVALID_ARG, "fa_fwd_split: workspace must not overlap the inputs or outputs");
+    const int64_t n_mtiles = (sq + tc.block_m - 1) / tc.block_m;
+    const int64_t items_per_head = n_mtiles * nsplit;
+    const int64_t n_items = b * h * items_per_head;
+    const int64_t merge_blocks = (b * h * sq * (d / 8) + 255) / 256;
+    if (n_items > INT32_MAX - 8 || items_per_head > INT32_MAX || merge_blocks > INT32_MAX)
+        return fail(FA_ERR_TOO_LARGE, "fa_fwd_split: too many tiles for one launch");
+    p.n_mtiles = (int)n_mtiles;
+    p.items_per_head = (int)items_per_head;
+    p.n_items = (int)n_items;
+    p.grid = (int)(((n_items + 7) / 8) * 8);
+    p.nsplit = nsplit;
+    p.ws = (float*)workspace;
+
+    hipError_t e = fa::launch_fwd_split(dtype, (int)d, tc, p, (hipStream_t)stream);
+    if (e != hipSuccess) {
+        snprintf(g_err, sizeof g_err, "fa_fwd_split: launch failed: %s", hipGetErrorString(e));
         return FA_ERR_HIP;
     }
     g_err[0] = 0;

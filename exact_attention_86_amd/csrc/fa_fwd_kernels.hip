@@ -44,6 +44,7 @@ typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies, 32 CUs each
@@ -145,6 +146,16 @@ __device__ __forceinline__ void copy_1k(const void* sbase, uint32_t voff, uint32
                  : "memory", "m0", "scc");
 }
 
+// a pointer the compiler cannot prove wave-uniform, moved to scalar registers
+// (the caller knows it is uniform)
+__device__ __forceinline__ const void* uniform_ptr(const void* ptr)
+{
+    const uint64_t v = (uint64_t)(uintptr_t)ptr;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
 __device__ __forceinline__ void wait_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // s_waitcnt vmcnt(n) with expcnt/lgkmcnt left unconstrained (n < 16)
@@ -180,7 +191,10 @@ __device__ __forceinline__ void static_for(F&& f)
 // QB 32-row query blocks per wave: every K or V operand read from LDS feeds
 // QB matrix-core instructions.  QB = 1 keeps two waves per SIMD; QB = 2 halves
 // the LDS traffic per MFMA at one wave per SIMD (more registers per wave).
-template <int D, int BN, int NW, int QB, bool BF16, bool CAUSAL>
+// SPLIT: a work item is one part of a query tile's key range (split-KV); the
+// tile writes its partial O (normalised by its own row sum) and partial LSE in
+// fp32 to the workspace, and fa_combine merges the parts.
+template <int D, int BN, int NW, int QB, bool BF16, bool CAUSAL, bool SPLIT>
 __global__ void __launch_bounds__(NW * 64, QB == 1 ? 2 : 1)
 fa_fwd_16(Params p)
 {
@@ -242,7 +256,8 @@ fa_fwd_16(Params p)
     const uint32_t lbase = __builtin_amdgcn_readfirstlane(lds0 + w * DMA * 1024);
     auto copy_k = [&](auto j_tag, auto st_tag, int n0, bool full) {
         constexpr int J = decltype(j_tag)::value, ST = decltype(st_tag)::value;
-        const uint16_t* src = K + (size_t)n0 * D;
+        const void* src = K + (size_t)n0 * D;
+        if constexpr (SPLIT) src = uniform_ptr(src);
         if (full) {
             copy_1k<ST * 2 * TB + J * 1024>(src, dk[J], lbase);
         } else {
@@ -253,7 +268,8 @@ fa_fwd_16(Params p)
     };
     auto copy_v = [&](auto j_tag, auto st_tag, int n0, bool full) {
         constexpr int J = decltype(j_tag)::value, ST = decltype(st_tag)::value;
-        const uint16_t* src = V + (size_t)n0 * D;
+        const void* src = V + (size_t)n0 * D;
+        if constexpr (SPLIT) src = uniform_ptr(src);
         if (full) {
             copy_1k<ST * 2 * TB + TB + J * 1024>(src, dv[J], lbase);
         } else {
@@ -289,13 +305,22 @@ fa_fwd_16(Params p)
     for (int e = 0; e < 2; ++e)
         rv[e] = TB + v_row * RB + (((e * 4 + 2 * vhalf + (vc >> 1)) ^ swz_v(v_row)) << 4) + (vc & 1) * 8;
 
-    auto process = [&](const int mt) {
+    auto process = [&](const int mt, const int split) {
         const int q0 = mt * BM;
 
         // ---- key range of this tile and of this wave ----
         const int q_end = min(q0 + BM, sq);
         const int kv_end = CAUSAL ? min(q_end, sk) : sk;
         const int nkv = (kv_end + BN - 1) / BN;
+        // key tiles [t_lo, t_hi) of this work item: all of them, or part
+        // `split` of nsplit near-equal parts (possibly empty)
+        int t_lo = 0, t_hi = nkv;
+        if (SPLIT) {
+            // (the division runs on the vector unit; the values are uniform)
+            const int chunk = __builtin_amdgcn_readfirstlane((nkv + p.nsplit - 1) / p.nsplit);
+            t_lo = __builtin_amdgcn_readfirstlane(min(nkv, split * chunk));
+            t_hi = __builtin_amdgcn_readfirstlane(min(nkv, t_lo + chunk));
+        }
         const int wq_first = q0 + w * WR;
         const int wq_end = min(wq_first + WR, sq);
         const int w_kv_end = (wq_end <= wq_first) ? 0 : (CAUSAL ? min(wq_end, sk) : sk);
@@ -469,7 +494,7 @@ fa_fwd_16(Params p)
             constexpr int S = decltype(stage_tag)::value;
             wait_copies();
             __syncthreads();
-            const bool pf = t + 1 < nkv;
+            const bool pf = t + 1 < t_hi;
             const bool pf_full = pf && (t + 2) * BN <= sk;
             if (t < w_nkv && pf_full) {
                 compute(stage_tag, Stage<1>{}, t * BN);
@@ -479,15 +504,42 @@ fa_fwd_16(Params p)
             }
         };
 
-        issue_tile(Stage<0>{}, 0);
-        int t = 0;
-        for (; t + 1 < nkv; t += 2) {
+        if (t_lo < t_hi) issue_tile(Stage<0>{}, t_lo * BN);
+        int t = t_lo;
+        for (; t + 1 < t_hi; t += 2) {
             step(Stage<0>{}, t);
             step(Stage<1>{}, t + 1);
         }
-        if (t < nkv) step(Stage<0>{}, t);
+        if (t < t_hi) step(Stage<0>{}, t);
 
         // ---- epilogue: O = O^T / l, LSE = (m + log2 l) ln 2 ----
+        if constexpr (SPLIT) {
+            // partial results of key tiles [t_lo, t_hi) in fp32; a row that saw
+            // no key here gets O = 0 and LSE = -inf (weight 0 in the merge)
+            const size_t rows = (size_t)p.bh * sq;
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                const float l_tot = l_run[qb] + __shfl_xor(l_run[qb], 32);
+                if (qrow[qb] < sq) {
+                    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+                    const size_t r = (size_t)split * rows + (size_t)bh * sq + qrow[qb];
+                    float* orow = p.ws + r * D;
+#pragma unroll
+                    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                        for (int rb = 0; rb < 4; ++rb) {
+                            f32x4_t v4;
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) v4[e] = oacc[qb][dt][rb * 4 + e] * inv;
+                            *(f32x4_t*)(orow + dt * 32 + rb * 8 + g * 4) = v4;
+                        }
+                    if (g == 0)
+                        p.ws[(size_t)p.nsplit * rows * D + r] =
+                            l_tot > 0.f ? (m_run[qb] + __log2f(l_tot)) * kLn2 : -INFINITY;
+                }
+            }
+            return;
+        }
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
             const float l_tot = l_run[qb] + __shfl_xor(l_run[qb], 32);
@@ -507,12 +559,18 @@ fa_fwd_16(Params p)
         }
     };
 
+    if constexpr (SPLIT) {
+        // item = query tile (heaviest first when causal) x key-range part
+        const int mq = __builtin_amdgcn_readfirstlane(item / p.nsplit);
+        process(CAUSAL ? p.n_mtiles - 1 - mq : mq, item - mq * p.nsplit);
+        return;
+    }
     int mts[2];
     const int nt = item_tiles(p, item, mts);
-    process(mts[0]);
+    process(mts[0], 0);
     if (nt > 1) {
         __syncthreads();  // every wave is done with the LDS stages
-        process(mts[1]);
+        process(mts[1], 0);
     }
 }
 
@@ -920,7 +978,6 @@ fa_fwd_32(Params p)
     #pragma unroll
             for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
 
-        typedef float f32x4_t __attribute__((ext_vector_type(4)));
         f32x4_t kreg[CH], vreg[CH];
         auto load_tile = [&](int n0) {
     #pragma unroll
@@ -1057,6 +1114,53 @@ fa_fwd_32(Params p)
 }
 
 // ---------------------------------------------------------------------------
+// split-KV merge of the partial results: LSE = ln sum_p e^{LSE_p},
+// O = sum_p e^{LSE_p - LSE} O_p (page "05 · kernel 工程与四代演化", section 2.1,
+// lists the split-KV forward class; the weights are the parts' shares of the
+// row's softmax denominator)
+// ---------------------------------------------------------------------------
+// One thread per (row, 8 consecutive d values); the D/8 threads of a row read
+// its partial LSEs (cached).  Memory-bound: nsplit * (D + 1) fp32 in per row.
+template <int D, bool BF16>
+__global__ void __launch_bounds__(256)
+fa_combine(Params p)
+{
+    constexpr int TPR = D / 8;
+    const size_t rows = (size_t)p.bh * p.sq;
+    const size_t gid = (size_t)blockIdx.x * 256 + threadIdx.x;
+    const size_t row = gid / TPR;
+    if (row >= rows) return;
+    const int c8 = (int)(gid % TPR) * 8;
+    const int ns = p.nsplit;
+    const float* wl = p.ws + (size_t)ns * rows * D;
+    float m = -INFINITY;
+    for (int s = 0; s < ns; ++s) m = fmaxf(m, wl[(size_t)s * rows + row]);
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    float sum = 0.f;
+    if (m != -INFINITY) {
+        for (int s = 0; s < ns; ++s) {
+            const float wgt = expf(wl[(size_t)s * rows + row] - m);  // 0 for an empty part
+            sum += wgt;
+            const float* op = p.ws + ((size_t)s * rows + row) * D + c8;
+            const f32x4_t a = *(const f32x4_t*)op, b = *(const f32x4_t*)(op + 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                acc[e] += wgt * a[e];
+                acc[4 + e] += wgt * b[e];
+            }
+        }
+    }
+    const float inv = sum > 0.f ? 1.f / sum : 0.f;
+    u32x4_t out;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) out[e] = pack2(acc[2 * e] * inv, acc[2 * e + 1] * inv, BF16);
+    *(u32x4_t*)((uint16_t*)p.o + row * D + c8) = out;
+    if (c8 == 0) p.lse[row] = sum > 0.f ? m + logf(sum) : -INFINITY;
+}
+
+// ---------------------------------------------------------------------------
 // launch table
 // ---------------------------------------------------------------------------
 template <typename KernelT>
@@ -1069,8 +1173,21 @@ static hipError_t launch(KernelT kernel, int nw, const Params& p, hipStream_t st
 template <int D, int BN, int NW, int QB, bool BF16>
 static hipError_t launch16(const Params& p, hipStream_t s)
 {
-    if (p.causal) return launch(fa_fwd_16<D, BN, NW, QB, BF16, true>, NW, p, s);
-    return launch(fa_fwd_16<D, BN, NW, QB, BF16, false>, NW, p, s);
+    if (p.causal) return launch(fa_fwd_16<D, BN, NW, QB, BF16, true, false>, NW, p, s);
+    return launch(fa_fwd_16<D, BN, NW, QB, BF16, false, false>, NW, p, s);
+}
+
+// split-KV: the partial-result kernel, then the merge on the same stream
+template <int D, int BN, int NW, bool BF16>
+static hipError_t launch16split(const Params& p, hipStream_t s)
+{
+    const hipError_t e = p.causal ? launch(fa_fwd_16<D, BN, NW, 1, BF16, true, true>, NW, p, s)
+                                  : launch(fa_fwd_16<D, BN, NW, 1, BF16, false, true>, NW, p, s);
+    if (e != hipSuccess) return e;
+    const size_t threads = (size_t)p.bh * p.sq * (D / 8);
+    auto merge = fa_combine<D, BF16>;
+    hipLaunchKernelGGL(merge, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, p);
+    return hipGetLastError();
 }
 
 template <int D, int BN, bool BF16>
@@ -1124,6 +1241,42 @@ bool tile_config(int dtype, int d, int64_t bh, int64_t sq, int causal, TileConfi
     tc->qb = qb;
     tc->kind = kind;
     return true;
+}
+
+// split-KV uses the 4-wave kernel's tiles for every head size
+bool tile_config_split(int dtype, int d, TileConfig* tc)
+{
+    if (dtype != 1 && dtype != 2) return false;
+    int bn;
+    if (d == 64) bn = 128;
+    else if (d == 128) bn = 64;
+    else if (d == 256) bn = 32;
+    else return false;
+    tc->block_m = 128;
+    tc->block_n = bn;
+    tc->waves = 4;
+    tc->lds = 4 * bn * d * 2;
+    tc->qb = 1;
+    tc->kind = 0;
+    return true;
+}
+
+hipError_t launch_fwd_split(int dtype, int d, const TileConfig& tc, const Params& p, hipStream_t s)
+{
+    (void)tc;
+    switch (dtype) {
+    case 2:
+        if (d == 64) return launch16split<64, 128, 4, true>(p, s);
+        if (d == 128) return launch16split<128, 64, 4, true>(p, s);
+        if (d == 256) return launch16split<256, 32, 4, true>(p, s);
+        break;
+    case 1:
+        if (d == 64) return launch16split<64, 128, 4, false>(p, s);
+        if (d == 128) return launch16split<128, 64, 4, false>(p, s);
+        if (d == 256) return launch16split<256, 32, 4, false>(p, s);
+        break;
+    }
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_fwd(int dtype, int d, const TileConfig& tc, const Params& p, hipStream_t s)

@@ -23,6 +23,8 @@ struct Params {
     int items_per_head;  // work items per head (causal: tile pairs)
     int n_items;         // bh * items_per_head
     int grid;            // workgroups launched
+    int nsplit;          // split-KV parts per query tile (1: no split)
+    float* ws;           // split-KV workspace: O parts [nsplit][bh][sq][d], then LSE parts [nsplit][bh][sq]
 };
 
 struct TileConfig {
@@ -33,5 +35,7 @@ struct TileConfig {
 
 bool tile_config(int dtype, int d, int64_t bh, int64_t sq, int causal, TileConfig* tc);
 hipError_t launch_fwd(int dtype, int d, const TileConfig& tc, const Params& p, hipStream_t stream);
+bool tile_config_split(int dtype, int d, TileConfig* tc);
+hipError_t launch_fwd_split(int dtype, int d, const TileConfig& tc, const Params& p, hipStream_t stream);
 
 }  // namespace fa

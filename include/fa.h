@@ -20,6 +20,7 @@
 #ifndef FA_H
 #define FA_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -97,6 +98,45 @@ FA_API int fa_fwd(const void* q, const void* k, const void* v, void* o,
 FA_API int fa_query_config(int dtype, int64_t d, int causal, int64_t b, int64_t h,
                            int64_t sq, int64_t sk, int* block_m, int* block_n,
                            int* waves, int* lds);
+
+/*
+ * fa_fwd_split -- the same forward with each query tile's key range cut into
+ * nsplit near-equal parts that run as separate work items (split-KV), for
+ * problems with too few query tiles to fill the GPU (short prefills, few
+ * heads, decode-shaped sq << sk).  Page "05 · kernel 工程与四代演化", section
+ * 2.1, lists the split-KV forward as its own kernel class.  Each part writes
+ * its partial result (O_p normalised by its own row sum, LSE_p) in fp32 to the
+ * workspace; a second kernel on the same stream merges them:
+ *
+ *     LSE = ln sum_p exp(LSE_p),   O = sum_p exp(LSE_p - LSE) O_p
+ *
+ * (a part that sees no key of a row contributes LSE_p = -inf, weight 0).  O
+ * and LSE equal fa_fwd's up to rounding.
+ *
+ *   q ... dtype  as fa_fwd; dtype FA_F16 or FA_BF16, d = 64, 128 or 256
+ *   nsplit       parts per query tile, 1..FA_MAX_SPLIT; nsplit = 1 is exactly
+ *                fa_fwd (the workspace is not used and may be NULL)
+ *   workspace    device buffer of at least fa_split_workspace_bytes() bytes,
+ *                16-byte aligned, owned by the caller, not overlapping q, k,
+ *                v, o or lse; its contents on entry do not matter and are
+ *                scratch afterwards.  Calls that share a workspace must be
+ *                ordered (same stream, or synchronised).
+ *   workspace_bytes  its size in bytes
+ *
+ * Returns FA_OK or an fa_status code (FA_ERR_UNSUPPORTED for fp32 or another
+ * head size; FA_ERR_INVALID_ARG for nsplit out of range or a missing, small
+ * or overlapping workspace; FA_ERR_MISALIGNED for a misaligned workspace).
+ */
+#define FA_MAX_SPLIT 64
+FA_API int fa_fwd_split(const void* q, const void* k, const void* v, void* o,
+                        float* lse, int64_t b, int64_t h, int64_t sq, int64_t sk,
+                        int64_t d, float scale, int causal, int dtype, int nsplit,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* fa_split_workspace_bytes -- workspace size fa_fwd_split needs:
+ * nsplit * b * h * sq * (d + 1) * 4 bytes (partial O and LSE in fp32); 0 for
+ * nsplit = 1 and for invalid arguments.  Host only. */
+FA_API size_t fa_split_workspace_bytes(int64_t b, int64_t h, int64_t sq, int64_t d, int nsplit);
 
 /* fa_last_error -- message of the last failing call on this host thread
  * ("" if none).  The pointer stays valid until the next call on the thread. */

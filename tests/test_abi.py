@@ -19,6 +19,7 @@ HEADER = os.path.join(ROOT, "include", "fa.h")
 # fails validation before it could use them
 A = 1 << 40
 Q, K, V, O, L = A, A + (1 << 34), A + (2 << 34), A + (3 << 34), A + (4 << 34)
+WS = A + (5 << 34)
 
 
 def declared_symbols():
@@ -27,7 +28,8 @@ def declared_symbols():
 
 
 def test_header_declares_the_entry_points():
-    assert set(declared_symbols()) == {"fa_fwd", "fa_query_config", "fa_last_error", "fa_version"}
+    assert set(declared_symbols()) == {"fa_fwd", "fa_fwd_split", "fa_split_workspace_bytes",
+                                       "fa_query_config", "fa_last_error", "fa_version"}
 
 
 def test_library_loads_and_exports_every_declared_symbol():
@@ -139,3 +141,51 @@ def test_binding_has_no_cpu_fallback():
     src = open(os.path.join(ROOT, "exact_attention_86_amd", "__init__.py")).read()
     assert "oracle" not in src
     assert "torch.nn" not in src and "softmax" not in src and "matmul" not in src
+
+
+# ---- split-KV entry points ----
+
+def test_split_workspace_bytes():
+    # nsplit parts of fp32 O (d values) and LSE (1 value) per row
+    assert fa.fa_split_workspace_bytes(2, 3, 100, 128, 4) == 4 * 2 * 3 * 100 * 129 * 4
+    assert fa.fa_split_workspace_bytes(1, 1, 1, 64, 64) == 64 * 65 * 4
+    assert fa.fa_split_workspace_bytes(2, 3, 100, 128, 1) == 0
+    for args in [(0, 1, 1, 64, 2), (1, 1, 0, 64, 2), (1, 1, 1, 0, 2), (1, 1, 1, 64, 0), (1, 1, 1, 64, 65)]:
+        assert fa.fa_split_workspace_bytes(*args) == 0
+
+
+def call_split(**kw):
+    args = dict(q=Q, k=K, v=V, o=O, lse=L, b=1, h=1, sq=16, sk=16, d=128,
+                scale=0.125, causal=0, dtype=fa.FA_BF16, nsplit=2, workspace=WS,
+                workspace_bytes=1 << 30, stream=None)
+    args.update(kw)
+    return fa.fa_fwd_split(**args)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(nsplit=0), fa.FA_ERR_INVALID_ARG),
+    (dict(nsplit=65), fa.FA_ERR_INVALID_ARG),
+    (dict(q=0), fa.FA_ERR_INVALID_ARG),
+    (dict(lse=0), fa.FA_ERR_INVALID_ARG),
+    (dict(sk=0), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARG),
+    (dict(causal=3), fa.FA_ERR_INVALID_ARG),
+    (dict(dtype=fa.FA_F32), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=fa.FA_F32, d=64), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=7), fa.FA_ERR_UNSUPPORTED),
+    (dict(q=Q + 2), fa.FA_ERR_MISALIGNED),
+    (dict(o=Q), fa.FA_ERR_INVALID_ARG),
+    (dict(workspace=0), fa.FA_ERR_INVALID_ARG),
+    (dict(workspace=WS + 4), fa.FA_ERR_MISALIGNED),
+    (dict(workspace_bytes=2 * 16 * 129 * 4 - 1), fa.FA_ERR_INVALID_ARG),     # one byte short
+    (dict(workspace=Q), fa.FA_ERR_INVALID_ARG),                              # overlaps q
+    (dict(workspace=O - 64), fa.FA_ERR_INVALID_ARG),                         # runs into o
+    (dict(workspace=L), fa.FA_ERR_INVALID_ARG),                              # overlaps lse
+    (dict(nsplit=1, q=0), fa.FA_ERR_INVALID_ARG),                            # nsplit 1: fa_fwd's checks
+    (dict(nsplit=1, d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(sq=1 << 24, d=256), fa.FA_ERR_TOO_LARGE),
+])
+def test_split_invalid_arguments_rejected_before_launch(kw, code):
+    assert call_split(**kw) == code
+    assert fa.fa_last_error().startswith("fa_")

@@ -40,19 +40,19 @@ def scale32(scale):
     return float(np.float32(scale))
 
 
-def run_gpu(q, k, v, causal, scale):
+def run_gpu(q, k, v, causal, scale, nsplit=1):
     import torch
     qd, kd, vd = (t.cuda() for t in (q, k, v))
-    o, lse = fa.attention(qd, kd, vd, causal=causal, scale=scale)
+    o, lse = fa.attention(qd, kd, vd, causal=causal, scale=scale, nsplit=nsplit)
     torch.cuda.synchronize()
     return o, lse
 
 
-def compare_full(w: W.Workload, seed=None):
+def compare_full(w: W.Workload, seed=None, nsplit=1):
     q, k, v = W.make(w, seed)
     s = scale32(w.scale)
-    note(f"[parity] {w.name} b{w.b} h{w.h} sq{w.sq} sk{w.sk} d{w.d} {w.dtype} causal={w.causal}")
-    o, lse = run_gpu(q, k, v, w.causal, s)
+    note(f"[parity] {w.name} b{w.b} h{w.h} sq{w.sq} sk{w.sk} d{w.d} {w.dtype} causal={w.causal} nsplit={nsplit}")
+    o, lse = run_gpu(q, k, v, w.causal, s, nsplit)
     ro, rl = oracle.attn(q, k, v, s, w.causal)
     go = o.double().cpu().numpy()
     gl = lse.double().cpu().numpy()
@@ -243,3 +243,49 @@ def test_stream_argument(gpu):
     o2, l2 = fa.attention(q, k, v)
     torch.cuda.synchronize()
     assert torch.equal(o, o2) and torch.equal(lse, l2)
+
+
+# ---- split-KV forward (fa_fwd_split): same result as the definition ----
+SPLIT = [
+    # (dtype, b, h, sq, sk, d, causal, nsplit)
+    ("f16", 2, 8, 1024, 1024, 128, False, 4),    # the fp16 prefill workload's shape
+    ("bf16", 1, 2, 300, 300, 128, True, 3),
+    ("bf16", 2, 4, 16, 4000, 128, False, 8),     # decode-shaped: sq << sk
+    ("f16", 1, 2, 5, 2049, 64, True, 16),        # causal sq < sk: most parts see no key
+    ("bf16", 1, 2, 130, 100, 256, False, 8),     # more parts than key tiles
+    ("f16", 1, 3, 257, 129, 64, True, 2),
+    ("bf16", 1, 1, 1, 1, 128, False, 2),
+    ("f16", 1, 2, 200, 3000, 256, False, 64),
+]
+
+
+@pytest.mark.parametrize("case", SPLIT, ids=lambda c: "%s-b%dh%d-sq%d-sk%d-d%d-%s-split%d" % (
+    c[0], c[1], c[2], c[3], c[4], c[5], "causal" if c[6] else "full", c[7]))
+def test_split_kv_full_compare(case, gpu):
+    dt, b, h, sq, sk, d, causal, nsplit = case
+    compare_full(W.shape("split", dt, b, h, sq, sk, d, causal, seed=sq + 3 * sk), nsplit=nsplit)
+
+
+def test_split_one_part_is_fa_fwd(gpu):
+    import torch
+    w = W.shape("split1", "bf16", 1, 2, 200, 333, 128, True, seed=11)
+    q, k, v = (t.cuda() for t in W.make(w))
+    o1, l1 = fa.attention(q, k, v, causal=True, scale=scale32(w.scale))
+    o2, l2 = fa.attention(q, k, v, causal=True, scale=scale32(w.scale), nsplit=1)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_split_workspace_contents_do_not_matter(gpu):
+    import torch
+    w = W.shape("splitws", "f16", 1, 2, 100, 700, 128, False, seed=12)
+    q, k, v = (t.cuda() for t in W.make(w))
+    need = fa.fa_split_workspace_bytes(1, 2, 100, 128, 5)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    outs = []
+    for fill in (0xFF, 0x00):  # 0xFF bytes read as fp32 NaN
+        ws.fill_(fill)
+        outs.append(fa.attention(q, k, v, scale=scale32(w.scale), nsplit=5, workspace=ws))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    assert bool(torch.isfinite(outs[0][0]).all())
