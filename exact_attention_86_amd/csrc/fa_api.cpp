@@ -32,7 +32,7 @@ extern "C" {
 
 FA_API const char* fa_last_error(void) { return g_err; }
 
-FA_API int fa_version(void) { return 100; /* 0.1.0 */ }
+FA_API int fa_version(void) { return 200; /* 0.2.0: adds fa_fwd_split */ }
 
 FA_API int fa_query_config(int dtype, int64_t d, int causal, int64_t b, int64_t h, int64_t sq,
                            int64_t sk, int* block_m, int* block_n, int* waves, int* lds)

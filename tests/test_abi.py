@@ -40,7 +40,7 @@ def test_library_loads_and_exports_every_declared_symbol():
 
 
 def test_version():
-    assert fa.fa_version() >= 100
+    assert fa.fa_version() >= 200
 
 
 @pytest.mark.parametrize("dtype,d", [(fa.FA_F16, 64), (fa.FA_F16, 128), (fa.FA_F16, 256),
