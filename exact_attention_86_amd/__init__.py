@@ -12,8 +12,13 @@ raise.
                  workspace, workspace_bytes, stream)
         split-KV forward; fa_split_workspace_bytes(b, h, sq, d, nsplit) sizes
         its workspace
+    fa_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, batch, h, total_q,
+                  total_k, max_sq, d, scale, causal, dtype, stream)
+        packed variable-length sequences
     attention(q, k, v, causal=False, scale=None, out=None, lse=None, nsplit=1)
         convenience wrapper over torch device tensors [b, h, s, d]
+    attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_sq, causal=False, ...)
+        convenience wrapper over packed torch tensors [h, total, d]
 """
 from __future__ import annotations
 
@@ -69,6 +74,9 @@ def lib() -> ctypes.CDLL:
         L.fa_fwd_split.restype = ctypes.c_int
         L.fa_split_workspace_bytes.argtypes = [i64, i64, i64, i64, ctypes.c_int]
         L.fa_split_workspace_bytes.restype = ctypes.c_size_t
+        L.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
+                                    ctypes.c_float, ctypes.c_int, ctypes.c_int, vp]
+        L.fa_fwd_varlen.restype = ctypes.c_int
         _lib = L
         return L
 
@@ -109,6 +117,14 @@ def fa_fwd_split(q, k, v, o, lse, b, h, sq, sk, d, scale, causal, dtype, nsplit,
 def fa_split_workspace_bytes(b, h, sq, d, nsplit) -> int:
     """Workspace bytes fa_fwd_split needs (0 for nsplit = 1 or invalid sizes)."""
     return int(lib().fa_split_workspace_bytes(int(b), int(h), int(sq), int(d), int(nsplit)))
+
+
+def fa_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, batch, h, total_q, total_k,
+                  max_sq, d, scale, causal, dtype, stream) -> int:
+    """The variable-length C entry point: device addresses as ints, returns the status code."""
+    return lib().fa_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, int(batch), int(h),
+                               int(total_q), int(total_k), int(max_sq), int(d), float(scale),
+                               int(causal), int(dtype), stream)
 
 
 def _dtype_code(t) -> int:
@@ -159,6 +175,41 @@ def attention(q, k, v, causal: bool = False, scale: float | None = None, out=Non
         rc = fa_fwd_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                           b, h, sq, sk, d, scale, int(bool(causal)), _dtype_code(q), nsplit,
                           workspace.data_ptr(), nbytes, s.cuda_stream)
+    if rc != FA_OK:
+        raise FaError(rc, fa_last_error())
+    return out, lse
+
+
+def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_sq: int, causal: bool = False,
+                     scale: float | None = None, out=None, lse=None, stream=None):
+    """O [h, total_q, d], LSE [h, total_q] for packed sequences: q [h, total_q, d],
+    k/v [h, total_k, d] device tensors, cu_seqlens_* int32 device tensors of
+    batch + 1 offsets.  Returns without synchronising."""
+    import torch
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise FaError(FA_ERR_INVALID_ARG, "q, k, v must be 3-d [h, total, d]")
+    h, total_q, d = q.shape
+    total_k = k.shape[1]
+    if tuple(k.shape) != (h, total_k, d) or tuple(v.shape) != (h, total_k, d):
+        raise FaError(FA_ERR_INVALID_ARG, "k and v must be [h, total_k, d] matching q")
+    for t in (q, k, v, cu_seqlens_q, cu_seqlens_k):
+        if not (t.is_cuda and t.is_contiguous()):
+            raise FaError(FA_ERR_INVALID_ARG, "all tensors must be contiguous device tensors")
+    if cu_seqlens_q.dtype != torch.int32 or cu_seqlens_k.dtype != torch.int32:
+        raise FaError(FA_ERR_INVALID_ARG, "cu_seqlens must be int32")
+    if cu_seqlens_q.numel() != cu_seqlens_k.numel() or cu_seqlens_q.numel() < 2:
+        raise FaError(FA_ERR_INVALID_ARG, "cu_seqlens_q and cu_seqlens_k need batch + 1 entries each")
+    batch = cu_seqlens_q.numel() - 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((h, total_q), dtype=torch.float32, device=q.device)
+    s = stream if stream is not None else torch.cuda.current_stream(q.device)
+    rc = fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                       cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), batch, h, total_q, total_k,
+                       max_sq, d, scale, int(bool(causal)), _dtype_code(q), s.cuda_stream)
     if rc != FA_OK:
         raise FaError(rc, fa_last_error())
     return out, lse

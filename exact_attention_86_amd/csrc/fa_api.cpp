@@ -32,7 +32,7 @@ extern "C" {
 
 FA_API const char* fa_last_error(void) { return g_err; }
 
-FA_API int fa_version(void) { return 200; /* 0.2.0: adds fa_fwd_split */ }
+FA_API int fa_version(void) { return 300; /* 0.3.0: adds fa_fwd_varlen */ }
 
 FA_API int fa_query_config(int dtype, int64_t d, int causal, int64_t b, int64_t h, int64_t sq,
                            int64_t sk, int* block_m, int* block_n, int* waves, int* lds)
@@ -101,6 +101,8 @@ static int check_common(const char* who, const void* q, const void* k, const voi
     p->causal = causal;
     p->nsplit = 1;
     p->ws = nullptr;
+    p->cu_q = p->cu_k = nullptr;
+    p->total_q = p->total_k = 0;
     return FA_OK;
 }
 
@@ -187,6 +189,73 @@ FA_API int fa_fwd_split(const void* q, const void* k, const void* v, void* o, fl
     hipError_t e = fa::launch_fwd_split(dtype, (int)d, tc, p, (hipStream_t)stream);
     if (e != hipSuccess) {
         snprintf(g_err, sizeof g_err, "fa_fwd_split: launch failed: %s", hipGetErrorString(e));
+        return FA_ERR_HIP;
+    }
+    g_err[0] = 0;
+    return FA_OK;
+}
+
+FA_API int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                         const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int64_t batch,
+                         int64_t h, int64_t total_q, int64_t total_k, int64_t max_sq, int64_t d,
+                         float scale, int causal, int dtype, void* stream)
+{
+    if (!q || !k || !v || !o || !lse || !cu_seqlens_q || !cu_seqlens_k)
+        return fail(FA_ERR_INVALID_ARG, "fa_fwd_varlen: NULL pointer");
+    if (batch <= 0 || h <= 0 || total_q <= 0 || total_k <= 0 || max_sq <= 0 || d <= 0)
+        return fail(FA_ERR_INVALID_ARG, "fa_fwd_varlen: batch, h, total_q, total_k, max_sq and d must be >= 1");
+    if (max_sq > total_q) return fail(FA_ERR_INVALID_ARG, "fa_fwd_varlen: max_sq exceeds total_q");
+    if (!isfinite(scale)) return fail(FA_ERR_INVALID_ARG, "fa_fwd_varlen: scale must be finite");
+    if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARG, "fa_fwd_varlen: causal must be 0 or 1");
+    fa::TileConfig tc;
+    if (d > 4096 || !fa::tile_config_split(dtype, (int)d, &tc))
+        return fail(FA_ERR_UNSUPPORTED, "fa_fwd_varlen: fp16/bf16 with d = 64, 128 or 256 only");
+    if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u)
+        return fail(FA_ERR_MISALIGNED, "fa_fwd_varlen: q, k, v, o must be 16-byte aligned");
+    if (((uintptr_t)lse | (uintptr_t)cu_seqlens_q | (uintptr_t)cu_seqlens_k) & 3u)
+        return fail(FA_ERR_MISALIGNED, "fa_fwd_varlen: lse and the offset arrays must be 4-byte aligned");
+    const int64_t lim = INT32_MAX;
+    if (total_q * d > lim || total_k * d > lim || h > lim || batch > lim - 1)
+        return fail(FA_ERR_TOO_LARGE, "fa_fwd_varlen: a per-head slice exceeds 2^31-1 elements");
+    const size_t nq = (size_t)(h * total_q * d) * 2, nk = (size_t)(h * total_k * d) * 2;
+    const size_t nl = (size_t)(h * total_q) * 4;
+    if (overlap(o, nq, q, nq) || overlap(o, nq, k, nk) || overlap(o, nq, v, nk) ||
+        overlap(lse, nl, q, nq) || overlap(lse, nl, k, nk) || overlap(lse, nl, v, nk) ||
+        overlap(lse, nl, o, nq))
+        return fail(FA_ERR_INVALID_ARG, "fa_fwd_varlen: o and lse must not overlap the inputs or each other");
+    const int64_t tiles = (max_sq + tc.block_m - 1) / tc.block_m;
+    const int64_t items_per_head = batch * tiles;
+    const int64_t n_items = h * items_per_head;
+    if (items_per_head > lim || n_items > lim - 8)
+        return fail(FA_ERR_TOO_LARGE, "fa_fwd_varlen: too many tiles for one launch");
+
+    fa::Params p;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.o = o;
+    p.lse = lse;
+    p.bh = (int)h;
+    p.sq = (int)max_sq;
+    p.sk = (int)total_k;
+    const float a = fabsf(scale);
+    p.c = a > 0.f ? (float)((double)a * 1.4426950408889634) : 1e-30f;
+    p.qsign = scale < 0.f ? 0x80008000u : 0u;
+    p.causal = causal;
+    p.n_mtiles = (int)tiles;
+    p.items_per_head = (int)items_per_head;
+    p.n_items = (int)n_items;
+    p.grid = (int)(((n_items + 7) / 8) * 8);
+    p.nsplit = 1;
+    p.ws = nullptr;
+    p.cu_q = cu_seqlens_q;
+    p.cu_k = cu_seqlens_k;
+    p.total_q = (int)total_q;
+    p.total_k = (int)total_k;
+
+    hipError_t e = fa::launch_fwd_varlen(dtype, (int)d, p, (hipStream_t)stream);
+    if (e != hipSuccess) {
+        snprintf(g_err, sizeof g_err, "fa_fwd_varlen: launch failed: %s", hipGetErrorString(e));
         return FA_ERR_HIP;
     }
     g_err[0] = 0;

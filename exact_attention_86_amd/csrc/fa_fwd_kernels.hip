@@ -194,7 +194,9 @@ __device__ __forceinline__ void static_for(F&& f)
 // SPLIT: a work item is one part of a query tile's key range (split-KV); the
 // tile writes its partial O (normalised by its own row sum) and partial LSE in
 // fp32 to the workspace, and fa_combine merges the parts.
-template <int D, int BN, int NW, int QB, bool BF16, bool CAUSAL, bool SPLIT>
+// VARLEN: packed variable-length sequences; a work item is one query tile of
+// one sequence of one head, and every address is offset to that sequence.
+template <int D, int BN, int NW, int QB, bool BF16, bool CAUSAL, bool SPLIT, bool VARLEN = false>
 __global__ void __launch_bounds__(NW * 64, QB == 1 ? 2 : 1)
 fa_fwd_16(Params p)
 {
@@ -225,15 +227,31 @@ fa_fwd_16(Params p)
     const int lane = tid & 63;
     const int l32 = lane & 31;
     const int g = lane >> 5;
-    const int sq = p.sq, sk = p.sk;
+    int sq = p.sq, sk = p.sk;
+    size_t qoff = (size_t)bh * sq, koff = (size_t)bh * sk;  // first row of this slice
+    int vtile = 0;
+    if constexpr (VARLEN) {
+        // bh = head; item = sequence * (query tiles of the longest sequence) + tile.
+        // Offsets are clamped into [0, total] so malformed offsets cannot
+        // address outside the buffers.
+        const int seq = __builtin_amdgcn_readfirstlane(item / p.n_mtiles);
+        vtile = item - seq * p.n_mtiles;
+        const int q0s = min(max(p.cu_q[seq], 0), p.total_q), q1s = min(max(p.cu_q[seq + 1], q0s), p.total_q);
+        const int k0s = min(max(p.cu_k[seq], 0), p.total_k), k1s = min(max(p.cu_k[seq + 1], k0s), p.total_k);
+        sq = q1s - q0s;
+        sk = k1s - k0s;
+        if (vtile * BM >= sq || sk <= 0) return;  // the whole workgroup leaves together
+        qoff = (size_t)bh * p.total_q + q0s;
+        koff = (size_t)bh * p.total_k + k0s;
+    }
     const float c = p.c;  // |scale| * log2(e)
     constexpr float kRescaleThreshold = 8.f;  // lazy rescale: p <= 2^8
     constexpr float kRescaleLimit = 256.f;    // partial row sum that forces the exact max
 
-    const uint16_t* __restrict__ Q = (const uint16_t*)p.q + (size_t)bh * sq * D;
-    const uint16_t* __restrict__ K = (const uint16_t*)p.k + (size_t)bh * sk * D;
-    const uint16_t* __restrict__ V = (const uint16_t*)p.v + (size_t)bh * sk * D;
-    uint16_t* __restrict__ O = (uint16_t*)p.o + (size_t)bh * sq * D;
+    const uint16_t* __restrict__ Q = (const uint16_t*)p.q + qoff * D;
+    const uint16_t* __restrict__ K = (const uint16_t*)p.k + koff * D;
+    const uint16_t* __restrict__ V = (const uint16_t*)p.v + koff * D;
+    uint16_t* __restrict__ O = (uint16_t*)p.o + qoff * D;
 
     // ---- global -> LDS copies.  Copy j of wave w fills LDS chunks
     //      c = (w*DMA + j)*64 + lane: row c / CPR, physical chunk c % CPR,
@@ -257,7 +275,7 @@ fa_fwd_16(Params p)
     auto copy_k = [&](auto j_tag, auto st_tag, int n0, bool full) {
         constexpr int J = decltype(j_tag)::value, ST = decltype(st_tag)::value;
         const void* src = K + (size_t)n0 * D;
-        if constexpr (SPLIT) src = uniform_ptr(src);
+        if constexpr (SPLIT || VARLEN) src = uniform_ptr(src);
         if (full) {
             copy_1k<ST * 2 * TB + J * 1024>(src, dk[J], lbase);
         } else {
@@ -269,7 +287,7 @@ fa_fwd_16(Params p)
     auto copy_v = [&](auto j_tag, auto st_tag, int n0, bool full) {
         constexpr int J = decltype(j_tag)::value, ST = decltype(st_tag)::value;
         const void* src = V + (size_t)n0 * D;
-        if constexpr (SPLIT) src = uniform_ptr(src);
+        if constexpr (SPLIT || VARLEN) src = uniform_ptr(src);
         if (full) {
             copy_1k<ST * 2 * TB + TB + J * 1024>(src, dv[J], lbase);
         } else {
@@ -554,11 +572,17 @@ fa_fwd_16(Params p)
                         const uint32_t w1 = pack2(oacc[qb][dt][rb * 4 + 2] * inv, oacc[qb][dt][rb * 4 + 3] * inv, BF16);
                         *(u32x2_t*)(orow + dt * 32 + rb * 8 + g * 4) = u32x2_t{w0, w1};
                     }
-                if (g == 0) p.lse[(size_t)bh * sq + qrow[qb]] = (m_run[qb] + __log2f(l_tot)) * kLn2;
+                if (g == 0) p.lse[qoff + qrow[qb]] = (m_run[qb] + __log2f(l_tot)) * kLn2;
             }
         }
     };
 
+    if constexpr (VARLEN) {
+        // one query tile of one sequence; heaviest first when causal
+        const int ntiles = (sq + BM - 1) / BM;
+        process(CAUSAL ? ntiles - 1 - vtile : vtile, 0);
+        return;
+    }
     if constexpr (SPLIT) {
         // item = query tile (heaviest first when causal) x key-range part
         const int mq = __builtin_amdgcn_readfirstlane(item / p.nsplit);
@@ -1177,6 +1201,14 @@ static hipError_t launch16(const Params& p, hipStream_t s)
     return launch(fa_fwd_16<D, BN, NW, QB, BF16, false, false>, NW, p, s);
 }
 
+// variable-length sequences (4-wave kernel)
+template <int D, int BN, bool BF16>
+static hipError_t launch16varlen(const Params& p, hipStream_t s)
+{
+    if (p.causal) return launch(fa_fwd_16<D, BN, 4, 1, BF16, true, false, true>, 4, p, s);
+    return launch(fa_fwd_16<D, BN, 4, 1, BF16, false, false, true>, 4, p, s);
+}
+
 // split-KV: the partial-result kernel, then the merge on the same stream
 template <int D, int BN, int NW, bool BF16>
 static hipError_t launch16split(const Params& p, hipStream_t s)
@@ -1274,6 +1306,23 @@ hipError_t launch_fwd_split(int dtype, int d, const TileConfig& tc, const Params
         if (d == 64) return launch16split<64, 128, 4, false>(p, s);
         if (d == 128) return launch16split<128, 64, 4, false>(p, s);
         if (d == 256) return launch16split<256, 32, 4, false>(p, s);
+        break;
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_fwd_varlen(int dtype, int d, const Params& p, hipStream_t s)
+{
+    switch (dtype) {
+    case 2:
+        if (d == 64) return launch16varlen<64, 128, true>(p, s);
+        if (d == 128) return launch16varlen<128, 64, true>(p, s);
+        if (d == 256) return launch16varlen<256, 32, true>(p, s);
+        break;
+    case 1:
+        if (d == 64) return launch16varlen<64, 128, false>(p, s);
+        if (d == 128) return launch16varlen<128, 64, false>(p, s);
+        if (d == 256) return launch16varlen<256, 32, false>(p, s);
         break;
     }
     return hipErrorInvalidValue;

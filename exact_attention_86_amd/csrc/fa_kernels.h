@@ -25,6 +25,9 @@ struct Params {
     int grid;            // workgroups launched
     int nsplit;          // split-KV parts per query tile (1: no split)
     float* ws;           // split-KV workspace: O parts [nsplit][bh][sq][d], then LSE parts [nsplit][bh][sq]
+    const int* cu_q;     // varlen: sequence offsets into the packed query rows (batch + 1)
+    const int* cu_k;     // varlen: sequence offsets into the packed key rows (batch + 1)
+    int total_q, total_k;  // varlen: packed rows per head
 };
 
 struct TileConfig {
@@ -36,6 +39,7 @@ struct TileConfig {
 bool tile_config(int dtype, int d, int64_t bh, int64_t sq, int causal, TileConfig* tc);
 hipError_t launch_fwd(int dtype, int d, const TileConfig& tc, const Params& p, hipStream_t stream);
 bool tile_config_split(int dtype, int d, TileConfig* tc);
+hipError_t launch_fwd_varlen(int dtype, int d, const Params& p, hipStream_t stream);
 hipError_t launch_fwd_split(int dtype, int d, const TileConfig& tc, const Params& p, hipStream_t stream);
 
 }  // namespace fa

@@ -138,6 +138,43 @@ FA_API int fa_fwd_split(const void* q, const void* k, const void* v, void* o,
  * nsplit = 1 and for invalid arguments.  Host only. */
 FA_API size_t fa_split_workspace_bytes(int64_t b, int64_t h, int64_t sq, int64_t d, int nsplit);
 
+/*
+ * fa_fwd_varlen -- the same forward over a batch of packed sequences of
+ * different lengths (page "05 · kernel 工程与四代演化", section 6.1, lists
+ * the variable-length forward among the exported entry points).  Each head
+ * stores its sequences back to back along the row axis:
+ *
+ *   q, o   [h, total_q, d] contiguous, dtype; sequence i owns query rows
+ *          cu_seqlens_q[i] .. cu_seqlens_q[i+1]-1 of every head
+ *   k, v   [h, total_k, d] contiguous, dtype; sequence i owns key rows
+ *          cu_seqlens_k[i] .. cu_seqlens_k[i+1]-1
+ *   lse    [h, total_q] fp32
+ *
+ * and every sequence is an independent attention problem (queries of
+ * sequence i attend only to keys of sequence i; causal: local key j attends
+ * to local query r iff j <= r, top-left as in fa_fwd).
+ *
+ *   cu_seqlens_q, cu_seqlens_k  device int32 arrays of batch + 1 offsets,
+ *          starting at 0, non-decreasing, ending at total_q / total_k
+ *   batch  number of sequences (>= 1)
+ *   max_sq an upper bound of the query lengths (sets the grid; rows of a
+ *          sequence past max_sq are not computed)
+ *   d      64, 128 or 256; dtype FA_F16 or FA_BF16
+ *
+ * A sequence with no query rows is skipped; every sequence with query rows
+ * needs at least one key (otherwise its rows are left unwritten).  The offset
+ * arrays live on the device, so their contents are not checked on the host;
+ * the kernel clamps them into [0, total] so malformed offsets cannot address
+ * outside the buffers (the results are then unspecified).  Returns FA_OK or an
+ * fa_status code as fa_fwd.
+ */
+FA_API int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o,
+                         float* lse, const int32_t* cu_seqlens_q,
+                         const int32_t* cu_seqlens_k, int64_t batch, int64_t h,
+                         int64_t total_q, int64_t total_k, int64_t max_sq,
+                         int64_t d, float scale, int causal, int dtype,
+                         void* stream);
+
 /* fa_last_error -- message of the last failing call on this host thread
  * ("" if none).  The pointer stays valid until the next call on the thread. */
 FA_API const char* fa_last_error(void);

@@ -29,7 +29,8 @@ def declared_symbols():
 
 def test_header_declares_the_entry_points():
     assert set(declared_symbols()) == {"fa_fwd", "fa_fwd_split", "fa_split_workspace_bytes",
-                                       "fa_query_config", "fa_last_error", "fa_version"}
+                                       "fa_fwd_varlen", "fa_query_config", "fa_last_error",
+                                       "fa_version"}
 
 
 def test_library_loads_and_exports_every_declared_symbol():
@@ -40,7 +41,7 @@ def test_library_loads_and_exports_every_declared_symbol():
 
 
 def test_version():
-    assert fa.fa_version() >= 200
+    assert fa.fa_version() >= 300
 
 
 @pytest.mark.parametrize("dtype,d", [(fa.FA_F16, 64), (fa.FA_F16, 128), (fa.FA_F16, 256),
@@ -189,3 +190,40 @@ def call_split(**kw):
 def test_split_invalid_arguments_rejected_before_launch(kw, code):
     assert call_split(**kw) == code
     assert fa.fa_last_error().startswith("fa_")
+
+
+# ---- variable-length entry point ----
+CQ, CK = A + (6 << 34), A + (6 << 34) + 4096
+
+
+def call_varlen(**kw):
+    args = dict(q=Q, k=K, v=V, o=O, lse=L, cu_seqlens_q=CQ, cu_seqlens_k=CK, batch=3, h=2,
+                total_q=100, total_k=120, max_sq=50, d=128, scale=0.125, causal=0,
+                dtype=fa.FA_BF16, stream=None)
+    args.update(kw)
+    return fa.fa_fwd_varlen(**args)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), fa.FA_ERR_INVALID_ARG),
+    (dict(cu_seqlens_q=0), fa.FA_ERR_INVALID_ARG),
+    (dict(cu_seqlens_k=0), fa.FA_ERR_INVALID_ARG),
+    (dict(batch=0), fa.FA_ERR_INVALID_ARG),
+    (dict(total_q=0), fa.FA_ERR_INVALID_ARG),
+    (dict(total_k=0), fa.FA_ERR_INVALID_ARG),
+    (dict(max_sq=0), fa.FA_ERR_INVALID_ARG),
+    (dict(max_sq=101), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), fa.FA_ERR_INVALID_ARG),
+    (dict(causal=2), fa.FA_ERR_INVALID_ARG),
+    (dict(dtype=fa.FA_F32), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(q=Q + 8), fa.FA_ERR_MISALIGNED),
+    (dict(cu_seqlens_q=CQ + 2), fa.FA_ERR_MISALIGNED),
+    (dict(lse=L + 1), fa.FA_ERR_MISALIGNED),
+    (dict(o=Q + 16), fa.FA_ERR_INVALID_ARG),
+    (dict(lse=O), fa.FA_ERR_INVALID_ARG),
+    (dict(total_q=1 << 24, max_sq=16, d=256), fa.FA_ERR_TOO_LARGE),
+])
+def test_varlen_invalid_arguments_rejected_before_launch(kw, code):
+    assert call_varlen(**kw) == code
+    assert fa.fa_last_error().startswith("fa_fwd_varlen")

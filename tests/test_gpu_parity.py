@@ -289,3 +289,48 @@ def test_split_workspace_contents_do_not_matter(gpu):
     torch.cuda.synchronize()
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
     assert bool(torch.isfinite(outs[0][0]).all())
+
+
+# ---- variable-length packed sequences (fa_fwd_varlen) ----
+VARLEN = [
+    # (dtype, h, d, causal, query lengths, key lengths)
+    ("bf16", 2, 128, False, [100, 1, 300], [100, 50, 300]),
+    ("bf16", 2, 128, True, [130, 257, 64], [130, 300, 64]),
+    ("f16", 3, 64, True, [5, 0, 200], [7, 9, 150]),
+    ("f16", 1, 256, False, [33, 129], [300, 1]),
+]
+
+
+@pytest.mark.parametrize("case", VARLEN, ids=lambda c: "%s-h%d-d%d-%s-%s" % (
+    c[0], c[1], c[2], "causal" if c[3] else "full", "_".join(map(str, c[4]))))
+def test_varlen_per_sequence_compare(case, gpu):
+    import torch
+    dt, h, d, causal, qlens, klens = case
+    note(f"[parity-varlen] {case}")
+    qs, ks, vs = [], [], []
+    for i, (sq_i, sk_i) in enumerate(zip(qlens, klens)):
+        w = W.shape("varlen%d" % i, dt, 1, h, max(sq_i, 1), sk_i, d, causal, seed=100 * i + sq_i + sk_i)
+        q, k, v = W.make(w)
+        qs.append(q[:, :, :sq_i])
+        ks.append(k)
+        vs.append(v)
+    qp = torch.cat(qs, dim=2)[0].contiguous()
+    kp = torch.cat(ks, dim=2)[0].contiguous()
+    vp = torch.cat(vs, dim=2)[0].contiguous()
+    cq = torch.tensor(np.concatenate([[0], np.cumsum(qlens)]), dtype=torch.int32)
+    ck = torch.tensor(np.concatenate([[0], np.cumsum(klens)]), dtype=torch.int32)
+    s = scale32(1.0 / math.sqrt(d))
+    o, lse = fa.attention_varlen(qp.cuda(), kp.cuda(), vp.cuda(), cq.cuda(), ck.cuda(), max(qlens),
+                                 causal=causal, scale=s)
+    torch.cuda.synchronize()
+    go = o.double().cpu().numpy()
+    gl = lse.double().cpu().numpy()
+    for i in range(len(qlens)):
+        if qlens[i] == 0:
+            continue
+        q0, q1, k0, k1 = int(cq[i]), int(cq[i + 1]), int(ck[i]), int(ck[i + 1])
+        ro, rl = oracle.attn(qp[None, :, q0:q1], kp[None, :, k0:k1], vp[None, :, k0:k1], s, causal)
+        eo = float(np.max(np.abs(go[:, q0:q1] - ro[0])))
+        el = float(np.max(np.abs(gl[:, q0:q1] - rl[0])))
+        note(f"  seq {i}: sq={q1 - q0} sk={k1 - k0} O max-abs={eo:.3e} LSE max-abs={el:.3e}")
+        assert eo <= TOL_O[dt] and el <= TOL_LSE
