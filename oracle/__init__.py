@@ -44,6 +44,14 @@ MUTANTS = {
     "max_last": 9,
 }
 
+# deliberate mistakes of the backward (pin tests only)
+BWD_MUTANTS = {
+    "no_d": 1,
+    "dk_no_scale": 2,
+    "dv_uses_dp": 3,
+    "dq_uses_v": 4,
+}
+
 
 def build(force: bool = True) -> str:
     """Compile attn_oracle.c into liboracle.so with gcc; returns the path."""
@@ -75,9 +83,10 @@ def _load():
         lib.oracle_attn_probs.argtypes = [dp, dp, dp, dp, dp, dp] + dims
         lib.oracle_attn_online_kv_outer.argtypes = [dp, dp, dp, dp, dp] + dims + [i64, i64]
         lib.oracle_attn_online_q_outer.argtypes = [dp, dp, dp, dp, dp] + dims + [i64, i64]
+        lib.oracle_attn_bwd.argtypes = [dp, dp, dp, dp, dp, dp, dp] + dims + [ctypes.c_int, ctypes.c_int]
         for f in ("oracle_attn", "oracle_attn_mutant", "oracle_attn_rows",
                   "oracle_attn_probs", "oracle_attn_online_kv_outer",
-                  "oracle_attn_online_q_outer"):
+                  "oracle_attn_online_q_outer", "oracle_attn_bwd"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
         return lib
@@ -205,3 +214,23 @@ def attn_online_kv_outer(q, k, v, scale, causal=False, br=32, bc=32):
 def attn_online_q_outer(q, k, v, scale, causal=False, br=64, bc=64):
     """Online-softmax recurrence, query tile outer (unnormalised accumulator)."""
     return _online(_load().oracle_attn_online_q_outer, q, k, v, scale, causal, br, bc)
+
+
+def attn_bwd(q, k, v, dout, scale, causal=False, mutant=0, nthreads=None):
+    """Gradient of the definition: (dQ, dK, dV) of sum(O * dout), fp64.
+
+    ``mutant`` selects a deliberate mistake (BWD_MUTANTS); pin tests only."""
+    q, k, v, g = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(dout)
+    b, h, sq, sk, d = _shapes(q, k, v)
+    if g.shape != q.shape:
+        raise ValueError("dout must have q's shape")
+    dq = np.empty_like(q)
+    dk = np.empty_like(k)
+    dv = np.empty_like(v)
+    code = BWD_MUTANTS[mutant] if isinstance(mutant, str) else int(mutant)
+    rc = _load().oracle_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(dq), _ptr(dk), _ptr(dv),
+                                 b, h, sq, sk, d, _scale_f64(scale), int(bool(causal)), code,
+                                 int(nthreads or default_threads()))
+    if rc:
+        raise ValueError("oracle_attn_bwd rejected its arguments")
+    return dq, dk, dv

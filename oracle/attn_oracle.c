@@ -42,6 +42,11 @@
  *   oracle_attn_mutant   -- the naive definition with one deliberate,
  *                           selectable mistake; the pin tests use it to show
  *                           each plausible mistake fails at least one pin.
+ *   oracle_attn_bwd      -- the gradient of the definition: given dO, the
+ *                           derivatives dQ, dK, dV of sum(O * dO) (the pages
+ *                           name a backward kernel class but print no formula;
+ *                           this is the calculus of the forward definition),
+ *                           with an optional deliberate mistake for the pins.
  *
  * All arrays are fp64, contiguous, row-major: q,o [b,h,sq,d]; k,v [b,h,sk,d];
  * lse [b,h,sq].  Return value 0 on success, -1 on invalid arguments.
@@ -428,5 +433,119 @@ int oracle_attn_online_q_outer(const double* q, const double* k,
         }
     }
     free(st);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Backward: derivatives of L = sum_ij O_ij dO_ij with respect to Q, K, V.   */
+/* With P_ij the softmax probabilities of row i (0 for keys it may not see):  */
+/*   dV_j  = sum_i P_ij dO_i                                                 */
+/*   dP_ij = dO_i . v_j                                                      */
+/*   D_i   = sum_j P_ij dP_ij            (equals dO_i . O_i)                 */
+/*   dS_ij = P_ij (dP_ij - D_i)          (derivative through the softmax)   */
+/*   dQ_i  = scale sum_j dS_ij k_j,   dK_j = scale sum_i dS_ij q_i           */
+/* Heads run in parallel; each thread owns whole heads.                      */
+/* ------------------------------------------------------------------------ */
+
+enum {
+    BMUT_NONE = 0,
+    BMUT_NO_D = 1,          /* dS = P dP (the row term D forgotten)          */
+    BMUT_DK_NO_SCALE = 2,   /* dK misses the scale                           */
+    BMUT_DV_USES_DP = 3,    /* dV accumulates dP-weighted dO instead of P    */
+    BMUT_DQ_USES_V = 4      /* dQ sums dS_ij v_j instead of dS_ij k_j        */
+};
+
+typedef struct {
+    const double *q, *k, *v, *dout;
+    double *dq, *dk, *dv;
+    int64_t bh, sq, sk, d;
+    double scale;
+    int causal, mut, tid, nthreads, status;
+} bjob_t;
+
+static void* run_bwd(void* arg)
+{
+    bjob_t* J = (bjob_t*)arg;
+    const int64_t sq = J->sq, sk = J->sk, d = J->d;
+    double* s = (double*)malloc(sizeof(double) * (size_t)sk);
+    double* p = (double*)malloc(sizeof(double) * (size_t)sk);
+    double* dp = (double*)malloc(sizeof(double) * (size_t)sk);
+    double* oi = (double*)malloc(sizeof(double) * (size_t)d);
+    if (!s || !p || !dp || !oi) {
+        J->status = -1;
+        free(s); free(p); free(dp); free(oi);
+        return NULL;
+    }
+    for (int64_t hh = J->tid; hh < J->bh; hh += J->nthreads) {
+        const double* qh = J->q + hh * sq * d;
+        const double* kh = J->k + hh * sk * d;
+        const double* vh = J->v + hh * sk * d;
+        const double* gh = J->dout + hh * sq * d;
+        double* dqh = J->dq + hh * sq * d;
+        double* dkh = J->dk + hh * sk * d;
+        double* dvh = J->dv + hh * sk * d;
+        for (int64_t x = 0; x < sk * d; ++x) { dkh[x] = 0.0; dvh[x] = 0.0; }
+        for (int64_t i = 0; i < sq; ++i) {
+            const double* qi = qh + i * d;
+            const double* gi = gh + i * d;
+            (void)attend_row(qi, kh, vh, i, sk, d, J->scale, J->causal, MUT_NONE, s, oi, p);
+            const int64_t n = key_limit(i, sk, J->causal, MUT_NONE);
+            double Di = 0.0;
+            for (int64_t j = 0; j < n; ++j) {
+                dp[j] = dot(gi, vh + j * d, d);
+                Di += p[j] * dp[j];
+            }
+            double* dqi = dqh + i * d;
+            for (int64_t x = 0; x < d; ++x) dqi[x] = 0.0;
+            for (int64_t j = 0; j < n; ++j) {
+                const double ds = p[j] * (J->mut == BMUT_NO_D ? dp[j] : dp[j] - Di);
+                const double* kj = kh + j * d;
+                const double* vj = vh + j * d;
+                const double* src = (J->mut == BMUT_DQ_USES_V) ? vj : kj;
+                const double wv = (J->mut == BMUT_DV_USES_DP) ? dp[j] : p[j];
+                const double sk_ = (J->mut == BMUT_DK_NO_SCALE) ? 1.0 : J->scale;
+                double* dkj = dkh + j * d;
+                double* dvj = dvh + j * d;
+                for (int64_t x = 0; x < d; ++x) {
+                    dqi[x] += J->scale * ds * src[x];
+                    dkj[x] += sk_ * ds * qi[x];
+                    dvj[x] += wv * gi[x];
+                }
+            }
+        }
+    }
+    free(s); free(p); free(dp); free(oi);
+    return NULL;
+}
+
+int oracle_attn_bwd(const double* q, const double* k, const double* v,
+                    const double* dout, double* dq, double* dk, double* dv,
+                    int64_t b, int64_t h, int64_t sq, int64_t sk, int64_t d,
+                    double scale, int causal, int mutant, int nthreads)
+{
+    if (!q || !k || !v || !dout || !dq || !dk || !dv || bad_dims(b, h, sq, sk, d))
+        return -1;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    bjob_t jobs[256];
+    pthread_t th[256];
+    for (int t = 0; t < nthreads; ++t) {
+        bjob_t J;
+        memset(&J, 0, sizeof J);
+        J.q = q; J.k = k; J.v = v; J.dout = dout; J.dq = dq; J.dk = dk; J.dv = dv;
+        J.bh = b * h; J.sq = sq; J.sk = sk; J.d = d; J.scale = scale;
+        J.causal = causal ? 1 : 0; J.mut = mutant; J.tid = t; J.nthreads = nthreads;
+        jobs[t] = J;
+    }
+    int started = 0;
+    for (int t = 1; t < nthreads; ++t) {
+        if (pthread_create(&th[t], NULL, run_bwd, &jobs[t]) != 0) break;
+        started = t;
+    }
+    run_bwd(&jobs[0]);
+    for (int t = started + 1; t < nthreads; ++t) run_bwd(&jobs[t]);
+    for (int t = 1; t <= started; ++t) pthread_join(th[t], NULL);
+    for (int t = 0; t < nthreads; ++t)
+        if (jobs[t].status) return -1;
     return 0;
 }
