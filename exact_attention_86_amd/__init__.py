@@ -77,6 +77,11 @@ def lib() -> ctypes.CDLL:
         L.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
                                     ctypes.c_float, ctypes.c_int, ctypes.c_int, vp]
         L.fa_fwd_varlen.restype = ctypes.c_int
+        L.fa_bwd.argtypes = [vp] * 10 + [ctypes.c_size_t, i64, i64, i64, i64, i64,
+                                         ctypes.c_float, ctypes.c_int, ctypes.c_int, vp]
+        L.fa_bwd.restype = ctypes.c_int
+        L.fa_bwd_workspace_bytes.argtypes = [i64, i64, i64]
+        L.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
         _lib = L
         return L
 
@@ -125,6 +130,19 @@ def fa_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, batch, h, total_q
     return lib().fa_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, int(batch), int(h),
                                int(total_q), int(total_k), int(max_sq), int(d), float(scale),
                                int(causal), int(dtype), stream)
+
+
+def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, b, h, sq, sk, d,
+           scale, causal, dtype, stream) -> int:
+    """The backward C entry point: device addresses as ints, returns the status code."""
+    return lib().fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, int(workspace_bytes),
+                        int(b), int(h), int(sq), int(sk), int(d), float(scale), int(causal),
+                        int(dtype), stream)
+
+
+def fa_bwd_workspace_bytes(b, h, sq) -> int:
+    """Workspace bytes fa_bwd needs (0 for invalid sizes)."""
+    return int(lib().fa_bwd_workspace_bytes(int(b), int(h), int(sq)))
 
 
 def _dtype_code(t) -> int:
@@ -213,3 +231,43 @@ def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_sq: int, causal: b
     if rc != FA_OK:
         raise FaError(rc, fa_last_error())
     return out, lse
+
+
+def attention_bwd(q, k, v, out, lse, dout, causal: bool = False, scale: float | None = None,
+                  dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """dQ, dK, dV for torch device tensors: q, out, dout [b,h,sq,d], k/v
+    [b,h,sk,d], lse [b,h,sq] fp32 as attention() returned them for the same
+    causal and scale.  Outputs and the workspace are allocated with torch when
+    not given.  Returns (dQ, dK, dV) without synchronising."""
+    import torch
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise FaError(FA_ERR_INVALID_ARG, "q, k, v must be 4-d [b, h, s, d]")
+    b, h, sq, d = q.shape
+    sk = k.shape[2]
+    if tuple(k.shape) != (b, h, sk, d) or tuple(v.shape) != (b, h, sk, d):
+        raise FaError(FA_ERR_INVALID_ARG, "k and v must be [b, h, sk, d] matching q")
+    if tuple(out.shape) != tuple(q.shape) or tuple(dout.shape) != tuple(q.shape):
+        raise FaError(FA_ERR_INVALID_ARG, "out and dout must have q's shape")
+    if tuple(lse.shape) != (b, h, sq) or lse.dtype != torch.float32:
+        raise FaError(FA_ERR_INVALID_ARG, "lse must be fp32 [b, h, sq]")
+    for t in (q, k, v, out, lse, dout):
+        if not (t.is_cuda and t.is_contiguous()):
+            raise FaError(FA_ERR_INVALID_ARG, "all tensors must be contiguous device tensors")
+    if not (q.dtype == k.dtype == v.dtype == out.dtype == dout.dtype):
+        raise FaError(FA_ERR_INVALID_ARG, "q, k, v, out, dout must share a dtype")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    need = fa_bwd_workspace_bytes(b, h, sq)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    nbytes = workspace.numel() * workspace.element_size()
+    s = stream if stream is not None else torch.cuda.current_stream(q.device)
+    rc = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
+                lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
+                nbytes, b, h, sq, sk, d, scale, int(bool(causal)), _dtype_code(q), s.cuda_stream)
+    if rc != FA_OK:
+        raise FaError(rc, fa_last_error())
+    return dq, dk, dv

@@ -7,6 +7,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "fa.h"
 #include "fa_kernels.h"
 
@@ -32,7 +34,7 @@ extern "C" {
 
 FA_API const char* fa_last_error(void) { return g_err; }
 
-FA_API int fa_version(void) { return 300; /* 0.3.0: adds fa_fwd_varlen */ }
+FA_API int fa_version(void) { return 400; /* 0.4.0: adds fa_bwd */ }
 
 FA_API int fa_query_config(int dtype, int64_t d, int causal, int64_t b, int64_t h, int64_t sq,
                            int64_t sk, int* block_m, int* block_n, int* waves, int* lds)
@@ -256,6 +258,81 @@ FA_API int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, f
     hipError_t e = fa::launch_fwd_varlen(dtype, (int)d, p, (hipStream_t)stream);
     if (e != hipSuccess) {
         snprintf(g_err, sizeof g_err, "fa_fwd_varlen: launch failed: %s", hipGetErrorString(e));
+        return FA_ERR_HIP;
+    }
+    g_err[0] = 0;
+    return FA_OK;
+}
+
+FA_API size_t fa_bwd_workspace_bytes(int64_t b, int64_t h, int64_t sq)
+{
+    if (b <= 0 || h <= 0 || sq <= 0) return 0;
+    return (size_t)(b * h * sq) * 4;
+}
+
+FA_API int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                  const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                  int64_t b, int64_t h, int64_t sq, int64_t sk, int64_t d, float scale, int causal,
+                  int dtype, void* stream)
+{
+    if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace)
+        return fail(FA_ERR_INVALID_ARG, "fa_bwd: NULL pointer");
+    if (b <= 0 || h <= 0 || sq <= 0 || sk <= 0 || d <= 0)
+        return fail(FA_ERR_INVALID_ARG, "fa_bwd: b, h, sq, sk and d must be >= 1");
+    if (!isfinite(scale)) return fail(FA_ERR_INVALID_ARG, "fa_bwd: scale must be finite");
+    if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARG, "fa_bwd: causal must be 0 or 1");
+    if (d > 4096 || !fa::bwd_supported(dtype, (int)d))
+        return fail(FA_ERR_UNSUPPORTED, "fa_bwd: fp16/bf16 with d = 128 only");
+    if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)dout | (uintptr_t)dq |
+         (uintptr_t)dk | (uintptr_t)dv | (uintptr_t)workspace) & 15u)
+        return fail(FA_ERR_MISALIGNED, "fa_bwd: tensors and workspace must be 16-byte aligned");
+    if ((uintptr_t)lse & 3u) return fail(FA_ERR_MISALIGNED, "fa_bwd: lse must be 4-byte aligned");
+    const int64_t lim = INT32_MAX;
+    if (sq * d > lim || sk * d > lim || b * h > lim || b > lim || h > lim || b * h * sq > lim)
+        return fail(FA_ERR_TOO_LARGE, "fa_bwd: a per-head slice exceeds 2^31-1 elements");
+    const size_t need = fa_bwd_workspace_bytes(b, h, sq);
+    if (workspace_bytes < need)
+        return fail(FA_ERR_INVALID_ARG, "fa_bwd: workspace smaller than fa_bwd_workspace_bytes()");
+    const size_t nq = (size_t)(b * h * sq * d) * 2, nk = (size_t)(b * h * sk * d) * 2;
+    const size_t nl = (size_t)(b * h * sq) * 4;
+    // outputs and workspace: disjoint from every input and from each other
+    const void* in[6] = {q, k, v, o, dout, lse};
+    const size_t in_n[6] = {nq, nk, nk, nq, nq, nl};
+    const void* outs[4] = {dq, dk, dv, workspace};
+    const size_t out_n[4] = {nq, nk, nk, need};
+    for (int i = 0; i < 4; ++i) {
+        for (int j = 0; j < 6; ++j)
+            if (overlap(outs[i], out_n[i], in[j], in_n[j]))
+                return fail(FA_ERR_INVALID_ARG, "fa_bwd: dq, dk, dv and workspace must not overlap the inputs");
+        for (int j = i + 1; j < 4; ++j)
+            if (overlap(outs[i], out_n[i], outs[j], out_n[j]))
+                return fail(FA_ERR_INVALID_ARG, "fa_bwd: dq, dk, dv and workspace must not overlap each other");
+    }
+    const int64_t items = b * h * ((std::max(sq, sk) + 127) / 128);
+    if (items > lim - 8) return fail(FA_ERR_TOO_LARGE, "fa_bwd: too many tiles for one launch");
+
+    fa::BwdParams p;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.o = o;
+    p.dout = dout;
+    p.lse = lse;
+    p.dq = dq;
+    p.dk = dk;
+    p.dv = dv;
+    p.dvec = (float*)workspace;
+    p.bh = (int)(b * h);
+    p.sq = (int)sq;
+    p.sk = (int)sk;
+    p.c = (float)((double)scale * 1.4426950408889634);
+    p.scale = scale;
+    p.causal = causal;
+    p.items_per_head = 0;
+    p.n_items = 0;
+    hipError_t e = fa::launch_bwd(dtype, (int)d, p, (hipStream_t)stream);
+    if (e != hipSuccess) {
+        snprintf(g_err, sizeof g_err, "fa_bwd: launch failed: %s", hipGetErrorString(e));
         return FA_ERR_HIP;
     }
     g_err[0] = 0;

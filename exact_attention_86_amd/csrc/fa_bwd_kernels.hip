@@ -1,0 +1,580 @@
+// fa_bwd_kernels.hip -- exact attention backward for gfx950 (CDNA4).
+//
+// Gradients of L = sum(O * dO) for O = softmax(scale Q K^T) V (page
+// "flash-attn 实现 prefill 阶段", section 问题分析), recomputing the
+// probabilities from the row log-sum-exp the forward saved, so the sq x sk
+// matrices never reach HBM (the reason the forward returns LSE; page "05 ·
+// kernel 工程与四代演化", section 2.1, lists the backward as its own kernel
+// class).  With P_ij = exp(scale q_i.k_j - LSE_i):
+//   D_i   = dO_i . O_i                      (fa_bwd_dot)
+//   dV_j  = sum_i P_ij dO_i                 (fa_bwd_dkdv)
+//   dK_j  = scale sum_i dS_ij q_i           (fa_bwd_dkdv)
+//   dQ_i  = scale sum_j dS_ij k_j           (fa_bwd_dq)
+//   with dP_ij = dO_i . v_j and dS_ij = P_ij (dP_ij - D_i).
+//
+// fa_bwd_dkdv: one workgroup = 128 keys of one head, wave w owns keys
+// [32w, 32w+32) and holds their K and V rows in registers for the whole
+// query loop.  Per 64-query step the Q and dO tiles (and their LSE and D) are
+// staged in LDS, double buffered.  Scores are computed untransposed,
+// S = Q K^T, so in the 32x32 accumulator layout lane l holds one key (column
+// l%32) and 16 queries -- exactly the B operand that dV^T += dO^T P and
+// dK^T += Q^T dS need (lane = key, 8 queries per half-wave), so P and dS go
+// from the accumulators to the matrix cores without a trip through LDS.  The
+// A operands dO^T and Q^T come from 8-byte transpose reads of the same LDS
+// tiles, in the query order the accumulator layout implies.
+//
+// fa_bwd_dq: one workgroup = 128 queries of one head, wave w owns 32 queries
+// and holds their Q and dO rows in registers; K and V tiles of 64 keys are
+// staged in LDS, double buffered.  Here the scores are transposed, S^T = K Q^T
+// (lane = query, so LSE_i and D_i are one register each), and
+// dQ^T += K^T dS^T takes dS^T as the B operand and K^T from transpose reads.
+//
+// Recomputing S and dP in both kernels (7 products where 5 would do with
+// atomic dQ updates) keeps the result deterministic and needs no fp32 dQ
+// accumulator in HBM.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa_device.h"
+#include "fa_kernels.h"
+
+namespace fa {
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// 16-byte chunk swizzle for 256-byte rows that are read both as 16-byte row
+// fragments (16 consecutive rows at one logical chunk: the map is a bijection
+// on the low four row bits, so they cover the 16 chunk positions of a bank
+// line) and with 8-byte transpose reads (4 consecutive rows x 4 consecutive
+// chunks: row bits 0-1 move chunk bits 2-3, so the 4 rows fall in different
+// 4-chunk groups).
+__device__ __forceinline__ int swz_b(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+
+__device__ __forceinline__ float widen16(uint32_t bits, bool bf16)
+{
+    if (bf16) return __uint_as_float(bits << 16);
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+}
+
+// workgroup id -> (head slice, work item), spreading consecutive ids over the
+// XCDs so each XCD takes a contiguous, head-major run of items (its L2 then
+// sees the same head's tensors from many workgroups)
+__device__ __forceinline__ bool map_bwd_item(int n_items, int items_per_head, int& bh, int& item)
+{
+    const int id = blockIdx.x;
+    const int per = (n_items + kXcds - 1) / kXcds;
+    const int t = (id % kXcds) * per + id / kXcds;
+    if (t >= n_items) return false;
+    bh = t / items_per_head;
+    item = t - bh * items_per_head;
+    return true;
+}
+
+// A operand of a 32x32x16 product from two 8-byte transpose reads at LDS
+// byte addresses a0 and a1
+__device__ __forceinline__ u32x4_t tr_pair(const char* a0, const char* a1)
+{
+    const v4i16_t x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(a0));
+    const v4i16_t x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(a1));
+    return u32x4_t{__builtin_bit_cast(u32x2_t, x0)[0], __builtin_bit_cast(u32x2_t, x0)[1],
+                   __builtin_bit_cast(u32x2_t, x1)[0], __builtin_bit_cast(u32x2_t, x1)[1]};
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// D_i = dO_i . O_i in fp32, one row per D/8 lanes (16 bytes of each tensor
+// per lane)
+// ---------------------------------------------------------------------------
+template <int D, bool BF16>
+__global__ void __launch_bounds__(256)
+fa_bwd_dot(BwdParams p)
+{
+    constexpr int LPR = D / 8;        // lanes per row
+    constexpr int RPB = 256 / LPR;    // rows per workgroup
+    static_assert(LPR <= 64 && (LPR & (LPR - 1)) == 0, "row must fit one wave");
+    const size_t rows = (size_t)p.bh * p.sq;
+    const size_t row = (size_t)blockIdx.x * RPB + threadIdx.x / LPR;
+    const int ch = threadIdx.x % LPR;
+    float acc = 0.f;
+    if (row < rows) {
+        const u32x4_t a = *(const u32x4_t*)((const uint16_t*)p.dout + row * D + ch * 8);
+        const u32x4_t b = *(const u32x4_t*)((const uint16_t*)p.o + row * D + ch * 8);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            acc = __builtin_fmaf(widen16(a[e] & 0xffffu, BF16), widen16(b[e] & 0xffffu, BF16), acc);
+            acc = __builtin_fmaf(widen16(a[e] >> 16, BF16), widen16(b[e] >> 16, BF16), acc);
+        }
+    }
+#pragma unroll
+    for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+    if (row < rows && ch == 0) p.dvec[row] = acc;
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV: one workgroup per 128 keys of one head
+// ---------------------------------------------------------------------------
+template <int D, bool BF16, bool CAUSAL>
+__global__ void __launch_bounds__(256, 1)
+fa_bwd_dkdv(BwdParams p)
+{
+    static_assert(D == 128, "256-byte rows");
+    constexpr int NW = 4;                 // waves; wave w owns keys [32w, 32w+32)
+    constexpr int BN = 32 * NW;           // keys per workgroup
+    constexpr int BMQ = 64;               // queries per step (two 32-row blocks)
+    constexpr int RB = D * 2;             // bytes per row
+    constexpr int NKK = D / 16;           // k-steps of S and dP
+    constexpr int NDT = D / 32;           // 32-wide d tiles of dK^T, dV^T
+    constexpr int TQ = BMQ * RB;          // bytes of one Q or dO tile
+    constexpr int OFF_LSE = 2 * TQ;       // stage layout: Q | dO | LSE (log2) | D
+    constexpr int OFF_D = OFF_LSE + BMQ * 4;
+    constexpr int STAGE = OFF_D + BMQ * 4;
+    constexpr int DMA = TQ / 1024 / NW;   // 1 KiB copies per wave per tensor per step
+    static_assert(DMA * 1024 * NW == TQ, "tile must split evenly over waves");
+    __shared__ __attribute__((aligned(16))) char lds[2 * STAGE];
+
+    int bh, kt;
+    if (!map_bwd_item(p.n_items, p.items_per_head, bh, kt)) return;
+    const int tid = threadIdx.x;
+    const int w = tid >> 6;
+    const int lane = tid & 63;
+    const int l32 = lane & 31;
+    const int g = lane >> 5;
+    const int sq = p.sq, sk = p.sk;
+    const int n0 = kt * BN;
+    const float c = p.c;
+
+    const uint16_t* __restrict__ Q = (const uint16_t*)p.q + (size_t)bh * sq * D;
+    const uint16_t* __restrict__ dO = (const uint16_t*)p.dout + (size_t)bh * sq * D;
+    const float* __restrict__ LSE = p.lse + (size_t)bh * sq;
+    const float* __restrict__ DV = p.dvec + (size_t)bh * sq;
+    const uint16_t* __restrict__ K = (const uint16_t*)p.k + (size_t)bh * sk * D;
+    const uint16_t* __restrict__ V = (const uint16_t*)p.v + (size_t)bh * sk * D;
+
+    // this wave's keys: B operands of S = Q K^T and dP = dO V^T (lane = key,
+    // 8 d values per half-wave); keys past the end re-read the last key
+    const int key = n0 + 32 * w + l32;
+    u32x4_t kf[NKK], vf[NKK];
+    {
+        const size_t kr = (size_t)min(key, sk - 1) * D + 8 * g;
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+            kf[kk] = *(const u32x4_t*)(K + kr + 16 * kk);
+            vf[kk] = *(const u32x4_t*)(V + kr + 16 * kk);
+        }
+    }
+
+    // query steps: causal keys n0.. are seen by queries n0.. only
+    const int qs_begin = CAUSAL ? n0 / BMQ : 0;
+    const int qs_end = (sq + BMQ - 1) / BMQ;
+
+    // ---- global -> LDS copies of the Q and dO tiles.  Copy j of wave w fills
+    //      LDS chunks cc = (w*DMA + j)*64 + lane: row cc/16, physical chunk
+    //      cc%16, fetched from the swizzled logical chunk ----
+    const uint32_t lbase = __builtin_amdgcn_readfirstlane(lds_addr(lds) + w * DMA * 1024);
+    uint32_t cof[DMA];
+#pragma unroll
+    for (int j = 0; j < DMA; ++j) {
+        const int cc = (w * DMA + j) * 64 + lane;
+        const int row = cc >> 4, pch = cc & 15;
+        cof[j] = row * RB + ((pch ^ swz_b(row)) << 4);
+    }
+    auto issue = [&](auto st_tag, int q0) {
+        constexpr int ST = decltype(st_tag)::value;
+        const bool full = q0 + BMQ <= sq;
+        const void* qsrc = uniform_ptr(Q + (size_t)q0 * D);
+        const void* gsrc = uniform_ptr(dO + (size_t)q0 * D);
+        static_for<DMA>([&](auto j_tag) {
+            constexpr int J = decltype(j_tag)::value;
+            uint32_t off = cof[J];
+            if (!full) {  // rows past the last query re-read it (masked later)
+                const int cc = (w * DMA + J) * 64 + lane;
+                const int row = cc >> 4, pch = cc & 15;
+                off = min(row, sq - 1 - q0) * RB + ((pch ^ swz_b(row)) << 4);
+            }
+            copy_1k<ST * STAGE + J * 1024>(qsrc, off, lbase);
+            copy_1k<ST * STAGE + TQ + J * 1024>(gsrc, off, lbase);
+        });
+    };
+    // LSE (converted to log2 units) and D of a step's 64 rows: wave 0 fetches
+    // LSE, wave 1 fetches D, one row per lane, and writes them into the stage
+    // just before the barrier that publishes it
+    float pend = 0.f;
+    auto fetch_rows = [&](int q0) {
+        if (w < 2) {
+            const int r = min(q0 + lane, sq - 1);
+            pend = (w == 0) ? LSE[r] * kLog2e : DV[r];
+        }
+    };
+    auto store_rows = [&](int st) {
+        if (w < 2) *(float*)(lds + st * STAGE + OFF_LSE + w * BMQ * 4 + lane * 4) = pend;
+    };
+
+    // ---- per-lane LDS read offsets (bytes within a stage) ----
+    //  row fragments (A operand of S and dP): row l32, logical chunk 2kk + g
+    uint32_t rq[NKK];
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) rq[kk] = l32 * RB + (((2 * kk + g) ^ swz_b(l32)) << 4);
+    //  transpose reads (A operand of dV^T and dK^T): lane 4r + c of its 16-lane
+    //  group reads query row 8j + 4g + r, d = 32dt + 16*half + 4c
+    const int sub = lane & 15, tr_r = sub >> 2, tr_c = sub & 3, half = (lane >> 4) & 1;
+    uint32_t rt[2][NDT];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int row = 8 * j + 4 * g + tr_r;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+            rt[j][dt] = row * RB + (((4 * dt + 2 * half + (tr_c >> 1)) ^ swz_b(row)) << 4) + (tr_c & 1) * 8;
+    }
+
+    f32x16_t dva[NDT], dka[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            dva[dt][r] = 0.f;
+            dka[dt][r] = 0.f;
+        }
+
+    auto compute = [&](auto st_tag, int q0) {
+        constexpr int S = decltype(st_tag)::value;
+        const char* sb = lds + S * STAGE;
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            const int qbase = q0 + 32 * qb;  // first query of this 32-row block
+            if (qbase >= sq) break;
+            if (CAUSAL && qbase + 31 < n0 + 32 * w) continue;  // all its queries precede this wave's keys
+            const char* qblk = sb + qb * 32 * RB;
+
+            // ---- S = Q K^T and dP = dO V^T: lane = key, rows = queries ----
+            f32x16_t s, dp;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                s[r] = 0.f;
+                dp[r] = 0.f;
+            }
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk) {
+                const u32x4_t aq = *(const u32x4_t*)(qblk + rq[kk]);
+                const u32x4_t ag = *(const u32x4_t*)(qblk + TQ + rq[kk]);
+                s = mfma16(aq, kf[kk], s, BF16);
+                dp = mfma16(ag, vf[kk], dp, BF16);
+            }
+
+            // ---- P = exp2(c s - LSE log2 e), dS = P (dP - D); accumulator row
+            //      r holds query 8(r/4) + 4g + r%4 of the block ----
+            f32x4_t l4[4], d4[4];
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) {
+                l4[rb] = *(const f32x4_t*)(sb + OFF_LSE + (32 * qb + 8 * rb + 4 * g) * 4);
+                d4[rb] = *(const f32x4_t*)(sb + OFF_D + (32 * qb + 8 * rb + 4 * g) * 4);
+            }
+            const bool need_mask = (qbase + 32 > sq) || (CAUSAL && qbase < n0 + 32 * w + 31);
+            u32x4_t pp[2], dsp[2];
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+                float pr[2], dr[2];
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const int rr = r + e;
+                    float pv = fast_exp2(__builtin_fmaf(s[rr], c, -l4[rr >> 2][rr & 3]));
+                    if (need_mask) {
+                        const int query = qbase + (rr >> 2) * 8 + 4 * g + (rr & 3);
+                        if (query >= sq || (CAUSAL && key > query)) pv = 0.f;
+                    }
+                    pr[e] = pv;
+                    dr[e] = pv * (dp[rr] - d4[rr >> 2][rr & 3]);
+                }
+                pp[r >> 3][(r >> 1) & 3] = pack2(pr[0], pr[1], BF16);
+                dsp[r >> 3][(r >> 1) & 3] = pack2(dr[0], dr[1], BF16);
+            }
+
+            // ---- dV^T += dO^T P and dK^T += Q^T dS over this block's queries ----
+#pragma unroll
+            for (int kc = 0; kc < 2; ++kc) {
+                const char* base = qblk + kc * 16 * RB;
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt) {
+                    const u32x4_t ag = tr_pair(base + TQ + rt[0][dt], base + TQ + rt[1][dt]);
+                    dva[dt] = mfma16(ag, pp[kc], dva[dt], BF16);
+                    const u32x4_t aq = tr_pair(base + rt[0][dt], base + rt[1][dt]);
+                    dka[dt] = mfma16(aq, dsp[kc], dka[dt], BF16);
+                }
+            }
+        }
+    };
+
+    auto step = [&](auto st_tag, int t) {
+        constexpr int S = decltype(st_tag)::value;
+        store_rows(S);
+        wait_copies();
+        __syncthreads();  // stage S is complete; every wave is done with stage S^1
+        if (t + 1 < qs_end) {
+            issue(Stage<S ^ 1>{}, (t + 1) * BMQ);
+            fetch_rows((t + 1) * BMQ);
+        }
+        compute(st_tag, t * BMQ);
+    };
+
+    if (qs_begin < qs_end) {
+        issue(Stage<0>{}, qs_begin * BMQ);
+        fetch_rows(qs_begin * BMQ);
+    }
+    int t = qs_begin;
+    for (; t + 1 < qs_end; t += 2) {
+        step(Stage<0>{}, t);
+        step(Stage<1>{}, t + 1);
+    }
+    if (t < qs_end) step(Stage<0>{}, t);
+
+    // ---- epilogue: dV = (dV^T)^T, dK = scale (dK^T)^T; accumulator row r of
+    //      d tile dt is d = 32dt + 8(r/4) + 4g + r%4 ----
+    if (key < sk) {
+        uint16_t* dvrow = (uint16_t*)p.dv + ((size_t)bh * sk + key) * D;
+        uint16_t* dkrow = (uint16_t*)p.dk + ((size_t)bh * sk + key) * D;
+        const float sc = p.scale;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) {
+                const int d0 = 32 * dt + 8 * rb + 4 * g;
+                *(u32x2_t*)(dvrow + d0) = u32x2_t{pack2(dva[dt][4 * rb], dva[dt][4 * rb + 1], BF16),
+                                                  pack2(dva[dt][4 * rb + 2], dva[dt][4 * rb + 3], BF16)};
+                *(u32x2_t*)(dkrow + d0) = u32x2_t{pack2(dka[dt][4 * rb] * sc, dka[dt][4 * rb + 1] * sc, BF16),
+                                                  pack2(dka[dt][4 * rb + 2] * sc, dka[dt][4 * rb + 3] * sc, BF16)};
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dQ: one workgroup per 128 queries of one head
+// ---------------------------------------------------------------------------
+template <int D, bool BF16, bool CAUSAL>
+__global__ void __launch_bounds__(256, 2)
+fa_bwd_dq(BwdParams p)
+{
+    static_assert(D == 128, "256-byte rows");
+    constexpr int NW = 4;                 // waves; wave w owns queries [32w, 32w+32)
+    constexpr int BM = 32 * NW;           // queries per workgroup
+    constexpr int BN = 64;                // keys per step (two 32-key blocks)
+    constexpr int RB = D * 2;
+    constexpr int NKK = D / 16;
+    constexpr int NDT = D / 32;
+    constexpr int TK = BN * RB;           // bytes of one K or V tile
+    constexpr int STAGE = 2 * TK;         // stage layout: K | V
+    constexpr int DMA = TK / 1024 / NW;
+    static_assert(DMA * 1024 * NW == TK, "tile must split evenly over waves");
+    __shared__ __attribute__((aligned(16))) char lds[2 * STAGE];
+
+    int bh, item;
+    if (!map_bwd_item(p.n_items, p.items_per_head, bh, item)) return;
+    const int tid = threadIdx.x;
+    const int w = tid >> 6;
+    const int lane = tid & 63;
+    const int l32 = lane & 31;
+    const int g = lane >> 5;
+    const int sq = p.sq, sk = p.sk;
+    const float c = p.c;
+    const int mt = CAUSAL ? p.items_per_head - 1 - item : item;  // causal: heaviest tiles first
+    const int q0 = mt * BM;
+
+    const uint16_t* __restrict__ Q = (const uint16_t*)p.q + (size_t)bh * sq * D;
+    const uint16_t* __restrict__ dO = (const uint16_t*)p.dout + (size_t)bh * sq * D;
+    const uint16_t* __restrict__ K = (const uint16_t*)p.k + (size_t)bh * sk * D;
+    const uint16_t* __restrict__ V = (const uint16_t*)p.v + (size_t)bh * sk * D;
+
+    // this wave's queries: B operands of S^T = K Q^T and dP^T = V dO^T (lane =
+    // query); rows past the end re-read the last row and are never stored
+    const int wq = q0 + 32 * w;
+    const int qrow = wq + l32;
+    const int qr = min(qrow, sq - 1);
+    u32x4_t qf[NKK], gf[NKK];
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+        qf[kk] = *(const u32x4_t*)(Q + (size_t)qr * D + 16 * kk + 8 * g);
+        gf[kk] = *(const u32x4_t*)(dO + (size_t)qr * D + 16 * kk + 8 * g);
+    }
+    const float lse2 = p.lse[(size_t)bh * sq + qr] * kLog2e;
+    const float drow = p.dvec[(size_t)bh * sq + qr];
+
+    const int q_end = min(q0 + BM, sq);
+    const int kv_end = CAUSAL ? min(q_end, sk) : sk;
+    const int nkv = (kv_end + BN - 1) / BN;
+    const int w_kv_end = (wq >= sq) ? 0 : (CAUSAL ? min(min(wq + 32, sq), sk) : sk);
+
+    const uint32_t lbase = __builtin_amdgcn_readfirstlane(lds_addr(lds) + w * DMA * 1024);
+    uint32_t cof[DMA];
+#pragma unroll
+    for (int j = 0; j < DMA; ++j) {
+        const int cc = (w * DMA + j) * 64 + lane;
+        const int row = cc >> 4, pch = cc & 15;
+        cof[j] = row * RB + ((pch ^ swz_b(row)) << 4);
+    }
+    auto issue = [&](auto st_tag, int n0) {
+        constexpr int ST = decltype(st_tag)::value;
+        const bool full = n0 + BN <= sk;
+        const void* ksrc = uniform_ptr(K + (size_t)n0 * D);
+        const void* vsrc = uniform_ptr(V + (size_t)n0 * D);
+        static_for<DMA>([&](auto j_tag) {
+            constexpr int J = decltype(j_tag)::value;
+            uint32_t off = cof[J];
+            if (!full) {  // rows past the last key re-read it (masked)
+                const int cc = (w * DMA + J) * 64 + lane;
+                const int row = cc >> 4, pch = cc & 15;
+                off = min(row, sk - 1 - n0) * RB + ((pch ^ swz_b(row)) << 4);
+            }
+            copy_1k<ST * STAGE + J * 1024>(ksrc, off, lbase);
+            copy_1k<ST * STAGE + TK + J * 1024>(vsrc, off, lbase);
+        });
+    };
+
+    uint32_t rk[NKK];
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) rk[kk] = l32 * RB + (((2 * kk + g) ^ swz_b(l32)) << 4);
+    const int sub = lane & 15, tr_r = sub >> 2, tr_c = sub & 3, half = (lane >> 4) & 1;
+    uint32_t rt[2][NDT];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int row = 8 * j + 4 * g + tr_r;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+            rt[j][dt] = row * RB + (((4 * dt + 2 * half + (tr_c >> 1)) ^ swz_b(row)) << 4) + (tr_c & 1) * 8;
+    }
+
+    f32x16_t dqa[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dqa[dt][r] = 0.f;
+
+    auto compute = [&](auto st_tag, int n0) {
+        constexpr int S = decltype(st_tag)::value;
+        const char* sb = lds + S * STAGE;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            const int kbase = n0 + 32 * kb;
+            if (kbase >= w_kv_end) break;
+            const char* kblk = sb + kb * 32 * RB;
+
+            // ---- S^T = K Q^T and dP^T = V dO^T: lane = query, rows = keys ----
+            f32x16_t s, dp;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                s[r] = 0.f;
+                dp[r] = 0.f;
+            }
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk) {
+                const u32x4_t ak = *(const u32x4_t*)(kblk + rk[kk]);
+                const u32x4_t av = *(const u32x4_t*)(kblk + TK + rk[kk]);
+                s = mfma16(ak, qf[kk], s, BF16);
+                dp = mfma16(av, gf[kk], dp, BF16);
+            }
+
+            // ---- dS^T = P^T (dP^T - D); row r holds key 8(r/4) + 4g + r%4 ----
+            const bool need_mask = (kbase + 32 > sk) || (CAUSAL && kbase + 31 > wq);
+            u32x4_t dsp[2];
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+                float dr[2];
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const int rr = r + e;
+                    float pv = fast_exp2(__builtin_fmaf(s[rr], c, -lse2));
+                    if (need_mask) {
+                        const int kidx = kbase + (rr >> 2) * 8 + 4 * g + (rr & 3);
+                        if (kidx >= sk || (CAUSAL && kidx > qrow)) pv = 0.f;
+                    }
+                    dr[e] = pv * (dp[rr] - drow);
+                }
+                dsp[r >> 3][(r >> 1) & 3] = pack2(dr[0], dr[1], BF16);
+            }
+
+            // ---- dQ^T += K^T dS^T ----
+#pragma unroll
+            for (int kc = 0; kc < 2; ++kc) {
+                const char* base = kblk + kc * 16 * RB;
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt) {
+                    const u32x4_t ak = tr_pair(base + rt[0][dt], base + rt[1][dt]);
+                    dqa[dt] = mfma16(ak, dsp[kc], dqa[dt], BF16);
+                }
+            }
+        }
+    };
+
+    auto step = [&](auto st_tag, int t) {
+        constexpr int S = decltype(st_tag)::value;
+        wait_copies();
+        __syncthreads();
+        if (t + 1 < nkv) issue(Stage<S ^ 1>{}, (t + 1) * BN);
+        compute(st_tag, t * BN);
+    };
+
+    if (nkv > 0) issue(Stage<0>{}, 0);
+    int t = 0;
+    for (; t + 1 < nkv; t += 2) {
+        step(Stage<0>{}, t);
+        step(Stage<1>{}, t + 1);
+    }
+    if (t < nkv) step(Stage<0>{}, t);
+
+    if (qrow < sq) {
+        uint16_t* dqrow = (uint16_t*)p.dq + ((size_t)bh * sq + qrow) * D;
+        const float sc = p.scale;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) {
+                const int d0 = 32 * dt + 8 * rb + 4 * g;
+                *(u32x2_t*)(dqrow + d0) = u32x2_t{pack2(dqa[dt][4 * rb] * sc, dqa[dt][4 * rb + 1] * sc, BF16),
+                                                  pack2(dqa[dt][4 * rb + 2] * sc, dqa[dt][4 * rb + 3] * sc, BF16)};
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// host launch
+// ---------------------------------------------------------------------------
+namespace {
+
+int round8(int64_t n) { return (int)(((n + 7) / 8) * 8); }
+
+template <int D, bool BF16>
+hipError_t launch_bwd_t(BwdParams p, hipStream_t s)
+{
+    constexpr int RPB = 256 / (D / 8);
+    const int64_t rows = (int64_t)p.bh * p.sq;
+    hipLaunchKernelGGL((fa_bwd_dot<D, BF16>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, s, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+
+    p.items_per_head = (p.sk + 127) / 128;
+    p.n_items = p.bh * p.items_per_head;
+    auto dkdv = p.causal ? fa_bwd_dkdv<D, BF16, true> : fa_bwd_dkdv<D, BF16, false>;
+    hipLaunchKernelGGL(dkdv, dim3(round8(p.n_items)), dim3(256), 0, s, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+
+    p.items_per_head = (p.sq + 127) / 128;
+    p.n_items = p.bh * p.items_per_head;
+    auto dq = p.causal ? fa_bwd_dq<D, BF16, true> : fa_bwd_dq<D, BF16, false>;
+    hipLaunchKernelGGL(dq, dim3(round8(p.n_items)), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool bwd_supported(int dtype, int d) { return (dtype == 1 || dtype == 2) && d == 128; }
+
+hipError_t launch_bwd(int dtype, int d, const BwdParams& p, hipStream_t stream)
+{
+    if (d != 128) return hipErrorInvalidValue;
+    if (dtype == 2) return launch_bwd_t<128, true>(p, stream);
+    if (dtype == 1) return launch_bwd_t<128, false>(p, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace fa

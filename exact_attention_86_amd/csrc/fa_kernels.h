@@ -36,10 +36,33 @@ struct TileConfig {
     int kind;  // 0: one wave group; 1: two ping-pong wave groups
 };
 
+// Backward launch parameters (fa_bwd).
+struct BwdParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* o;
+    const void* dout;
+    const float* lse;    // forward row log-sum-exp, natural log, [bh][sq]
+    void* dq;
+    void* dk;
+    void* dv;
+    float* dvec;         // workspace: D_i = dO_i . O_i, [bh][sq] fp32
+    int bh;
+    int sq, sk;
+    float c;             // scale * log2(e), signed
+    float scale;
+    int causal;
+    int items_per_head;  // set per kernel by the launcher
+    int n_items;
+};
+
 bool tile_config(int dtype, int d, int64_t bh, int64_t sq, int causal, TileConfig* tc);
 hipError_t launch_fwd(int dtype, int d, const TileConfig& tc, const Params& p, hipStream_t stream);
 bool tile_config_split(int dtype, int d, TileConfig* tc);
 hipError_t launch_fwd_varlen(int dtype, int d, const Params& p, hipStream_t stream);
+bool bwd_supported(int dtype, int d);
+hipError_t launch_bwd(int dtype, int d, const BwdParams& p, hipStream_t stream);
 hipError_t launch_fwd_split(int dtype, int d, const TileConfig& tc, const Params& p, hipStream_t stream);
 
 }  // namespace fa

@@ -175,6 +175,51 @@ FA_API int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o,
                          int64_t d, float scale, int causal, int dtype,
                          void* stream);
 
+/*
+ * fa_bwd -- gradients of fa_fwd: given dout = dL/dO, writes dq = dL/dQ,
+ * dk = dL/dK and dv = dL/dV for O = softmax(scale Q K^T) V (page "flash-attn
+ * 实现 prefill 阶段", section 问题分析, differentiated; page "05 · kernel
+ * 工程与四代演化", section 2.1, lists the backward as its own kernel class and
+ * section 6.1 its export).  The probabilities are recomputed from the row LSE
+ * the forward returned, so no sq x sk matrix is stored:
+ *
+ *     P_ij  = exp(scale q_i.k_j - LSE_i)      (0 where causal masks j > i)
+ *     D_i   = dout_i . o_i
+ *     dS_ij = P_ij (dout_i . v_j - D_i)
+ *     dv_j  = sum_i P_ij dout_i
+ *     dk_j  = scale sum_i dS_ij q_i
+ *     dq_i  = scale sum_j dS_ij k_j
+ *
+ *   q, o, dout, dq   [b, h, sq, d] contiguous, dtype
+ *   k, v, dk, dv     [b, h, sk, d] contiguous, dtype
+ *   lse              [b, h, sq] fp32, as fa_fwd wrote it for these q, k, v,
+ *                    scale and causal (o likewise)
+ *   workspace        device buffer of at least fa_bwd_workspace_bytes()
+ *                    bytes (holds D in fp32), 16-byte aligned, owned by the
+ *                    caller; contents on entry do not matter.  Calls that
+ *                    share a workspace must be ordered (same stream).
+ *   workspace_bytes  its size in bytes
+ *   d                128;  dtype FA_F16 or FA_BF16
+ *   scale, causal    as passed to fa_fwd
+ *   stream           hipStream_t; three kernels are enqueued on it
+ *
+ * dq, dk, dv and the workspace must not overlap the inputs or each other.
+ * P and dS are rounded to dtype before they enter the matrix cores (fp32
+ * accumulation).  Deterministic: no atomics, the same inputs give the same
+ * bits.  Returns FA_OK or an fa_status code as fa_fwd (FA_ERR_UNSUPPORTED for
+ * fp32 or d != 128; FA_ERR_INVALID_ARG for a missing, small or overlapping
+ * workspace).
+ */
+FA_API int fa_bwd(const void* q, const void* k, const void* v, const void* o,
+                  const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                  void* workspace, size_t workspace_bytes, int64_t b, int64_t h,
+                  int64_t sq, int64_t sk, int64_t d, float scale, int causal,
+                  int dtype, void* stream);
+
+/* fa_bwd_workspace_bytes -- workspace size fa_bwd needs: b * h * sq * 4
+ * bytes; 0 for invalid arguments.  Host only. */
+FA_API size_t fa_bwd_workspace_bytes(int64_t b, int64_t h, int64_t sq);
+
 /* fa_last_error -- message of the last failing call on this host thread
  * ("" if none).  The pointer stays valid until the next call on the thread. */
 FA_API const char* fa_last_error(void);

@@ -30,7 +30,7 @@ def declared_symbols():
 def test_header_declares_the_entry_points():
     assert set(declared_symbols()) == {"fa_fwd", "fa_fwd_split", "fa_split_workspace_bytes",
                                        "fa_fwd_varlen", "fa_query_config", "fa_last_error",
-                                       "fa_version"}
+                                       "fa_version", "fa_bwd", "fa_bwd_workspace_bytes"}
 
 
 def test_library_loads_and_exports_every_declared_symbol():
@@ -41,7 +41,7 @@ def test_library_loads_and_exports_every_declared_symbol():
 
 
 def test_version():
-    assert fa.fa_version() >= 300
+    assert fa.fa_version() >= 400
 
 
 @pytest.mark.parametrize("dtype,d", [(fa.FA_F16, 64), (fa.FA_F16, 128), (fa.FA_F16, 256),
@@ -227,3 +227,59 @@ def call_varlen(**kw):
 def test_varlen_invalid_arguments_rejected_before_launch(kw, code):
     assert call_varlen(**kw) == code
     assert fa.fa_last_error().startswith("fa_fwd_varlen")
+
+
+# ---- backward ----
+DO, DQ, DK, DV = A + (7 << 34), A + (8 << 34), A + (9 << 34), A + (10 << 34)
+
+
+def test_bwd_workspace_bytes():
+    assert fa.fa_bwd_workspace_bytes(2, 3, 100) == 2 * 3 * 100 * 4
+    for args in [(0, 1, 1), (1, 0, 1), (1, 1, 0)]:
+        assert fa.fa_bwd_workspace_bytes(*args) == 0
+
+
+def call_bwd(**kw):
+    args = dict(q=Q, k=K, v=V, o=O, dout=DO, lse=L, dq=DQ, dk=DK, dv=DV, workspace=WS,
+                workspace_bytes=1 << 30, b=1, h=2, sq=40, sk=50, d=128, scale=0.125, causal=0,
+                dtype=fa.FA_BF16, stream=None)
+    args.update(kw)
+    return fa.fa_bwd(**args)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), fa.FA_ERR_INVALID_ARG),
+    (dict(dout=0), fa.FA_ERR_INVALID_ARG),
+    (dict(lse=0), fa.FA_ERR_INVALID_ARG),
+    (dict(dv=0), fa.FA_ERR_INVALID_ARG),
+    (dict(workspace=0), fa.FA_ERR_INVALID_ARG),
+    (dict(sq=0), fa.FA_ERR_INVALID_ARG),
+    (dict(sk=0), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARG),
+    (dict(causal=2), fa.FA_ERR_INVALID_ARG),
+    (dict(dtype=fa.FA_F32), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=64), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=256), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=9), fa.FA_ERR_UNSUPPORTED),
+    (dict(dq=DQ + 8), fa.FA_ERR_MISALIGNED),
+    (dict(workspace=WS + 4), fa.FA_ERR_MISALIGNED),
+    (dict(lse=L + 2), fa.FA_ERR_MISALIGNED),
+    (dict(workspace_bytes=2 * 40 * 4 - 1), fa.FA_ERR_INVALID_ARG),    # one byte short
+    (dict(dq=Q), fa.FA_ERR_INVALID_ARG),                               # output over an input
+    (dict(dk=L - 64), fa.FA_ERR_INVALID_ARG),                          # runs into lse
+    (dict(dv=DK + 16), fa.FA_ERR_INVALID_ARG),                         # outputs overlap
+    (dict(workspace=DQ + 1024), fa.FA_ERR_INVALID_ARG),                # workspace inside dq
+    (dict(sq=1 << 24, d=128), fa.FA_ERR_TOO_LARGE),
+])
+def test_bwd_invalid_arguments_rejected_before_launch(kw, code):
+    assert call_bwd(**kw) == code
+    assert fa.fa_last_error().startswith("fa_bwd")
+
+
+def test_bwd_binding_rejects_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 1, 4, 128, dtype=torch.bfloat16)
+    lse = torch.zeros(1, 1, 4)
+    with pytest.raises(fa.FaError):
+        fa.attention_bwd(x, x, x, x, lse, x)
+

@@ -123,3 +123,14 @@ def make(w: Workload, seed: int | None = None):
 
 def with_(w: Workload, **kw) -> Workload:
     return replace(w, **kw)
+
+
+def make_dout(w: Workload, seed: int | None = None):
+    """The output gradient dO for a backward pass: i.i.d. standard normal
+    [b, h, sq, d] from its own generator (seed + 7919), fp64 -> fp32 -> the
+    workload dtype, as a CPU torch tensor."""
+    import torch
+    rng = np.random.default_rng((w.seed if seed is None else seed) + 7919)
+    g = rng.standard_normal((w.b, w.h, w.sq, w.d), dtype=np.float64).astype(np.float32)
+    return torch.from_numpy(g).to(_torch_dtype(w.dtype))
+
