@@ -1,13 +1,17 @@
 """Throughput of the exact-attention prefill forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--split N] [--no-cpu-baseline]
+                    [--split N | --bwd] [--no-cpu-baseline]
 
 One step is one fa_fwd call (the whole hot path: tile schedule, Q/K/V tile
 loads, S = QK^T, masking, online softmax, O += PV, epilogue) over the
 workload's synthetic inputs, which are resident in HBM before timing starts.
 With --split N > 1 a step is one fa_fwd_split call (split-KV forward plus the
-merge kernel; the workspace is allocated before timing).
+merge kernel; the workspace is allocated before timing).  With --bwd a step
+is one fa_bwd call (the D = dO.O pass, the dK/dV kernel and the dQ kernel)
+on O and LSE that one fa_fwd call produced before timing; its FLOP count is
+the usual 2.5x the forward's (five sq x sk x d products where the forward has
+two), and the roofline covers the three kernels of the call together.
 Warm-up runs at least W steps and at least 0.5 s of launches (clocks settle).
 Prints ONE JSON line.  ``value`` is TFLOP/s with the usual attention count
 4*b*h*sq*sk*d (halved when causal) over the wall-clock of the K timed steps;
@@ -35,11 +39,12 @@ import numpy as np  # noqa: E402
 import workloads as W  # noqa: E402
 
 METRIC = "attn fwd TFLOP/s, b4 h32 sq4096 d128 bf16 causal; % of MFMA peak"
+METRIC_BWD = "attn bwd TFLOP/s (2.5x fwd FLOP count), b4 h32 sq4096 d128 bf16 causal; % of MFMA peak"
 # MI355X dense matrix peaks (TFLOP/s): 256 CUs x 2.4 GHz x FLOP/clk/CU
 PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}
 PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_86_amd", "csrc", f)
-                  for f in ("fa_fwd_kernels.hip", "fa_kernels.h", "fa_api.cpp")]
+                  for f in ("fa_fwd_kernels.hip", "fa_device.h", "fa_kernels.h", "fa_api.cpp")]
 
 
 def log(*a):
@@ -95,6 +100,30 @@ def cpu_baseline(w: W.Workload, q, k, v, budget_s: float):
                 nheads, w.b * w.h, w.sq, w.sk, dt)}
 
 
+def cpu_baseline_bwd(w: W.Workload, q, k, v, budget_s: float):
+    """Time the oracle's backward on whole heads (about budget_s of CPU work;
+    the oracle threads over heads, so at least one head per thread) and scale
+    to TFLOP/s with the backward FLOP convention."""
+    import oracle
+    nthreads = oracle.default_threads()
+    scale = float(np.float32(w.scale))
+    g = W.make_dout(w)
+    head_flops = 2.5 * w.flops / (w.b * w.h)
+    t0 = time.perf_counter()
+    oracle.attn_bwd(q[0:1, 0:1], k[0:1, 0:1], v[0:1, 0:1], g[0:1, 0:1], scale, w.causal, nthreads=1)
+    t1 = time.perf_counter() - t0
+    per_round = max(t1, 1e-3)  # one head per thread runs in about t1
+    nheads = int(max(1, min(w.b * w.h - 1, nthreads * max(1, int(budget_s / per_round)))))
+    sl = lambda t, s: t.reshape(1, w.b * w.h, s, w.d)[:, 1:1 + nheads]
+    t0 = time.perf_counter()
+    oracle.attn_bwd(sl(q, w.sq), sl(k, w.sk), sl(v, w.sk), sl(g, w.sq), scale, w.causal, nthreads=nthreads)
+    dt = time.perf_counter() - t0
+    return {"value": head_flops * nheads / dt / 1e12, "unit": "TFLOP/s", "cores": min(nthreads, nheads),
+            "kind": "oracle",
+            "sample": "backward of %d of %d heads (full sq=%d x sk=%d each), fp64 C oracle, %.1f s" % (
+                nheads, w.b * w.h, w.sq, w.sk, dt)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -103,6 +132,8 @@ def main():
     ap.add_argument("--workload", default=W.HEADLINE.name, choices=sorted(W.BY_NAME))
     ap.add_argument("--split", type=int, default=1, metavar="N",
                     help="split-KV parts per query tile (fa_fwd_split); 1 = fa_fwd")
+    ap.add_argument("--bwd", action="store_true",
+                    help="time the backward (fa_bwd) instead of the forward")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -142,7 +173,26 @@ def main():
     code = W.DTYPE_CODE[w.dtype]
     ptrs = (qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), od.data_ptr(), lsed.data_ptr())
 
-    if args.split > 1:
+    if args.bwd and args.split > 1:
+        print("--bwd and --split are exclusive", file=sys.stderr)
+        sys.exit(2)
+    if args.bwd:
+        rc = fa.fa_fwd(*ptrs, w.b, w.h, w.sq, w.sk, w.d, scale, int(w.causal), code, stream.cuda_stream)
+        if rc != fa.FA_OK:
+            raise fa.FaError(rc, fa.fa_last_error())
+        gd = W.make_dout(w).to(dev)
+        dqd, dkd, dvd = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+        ws_bytes = fa.fa_bwd_workspace_bytes(w.b, w.h, w.sq)
+        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+        bptrs = (qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), od.data_ptr(), gd.data_ptr(),
+                 lsed.data_ptr(), dqd.data_ptr(), dkd.data_ptr(), dvd.data_ptr(), ws.data_ptr())
+
+        def step():
+            rc = fa.fa_bwd(*bptrs, ws_bytes, w.b, w.h, w.sq, w.sk, w.d, scale, int(w.causal), code,
+                           stream.cuda_stream)
+            if rc != fa.FA_OK:
+                raise fa.FaError(rc, fa.fa_last_error())
+    elif args.split > 1:
         ws_bytes = fa.fa_split_workspace_bytes(w.b, w.h, w.sq, w.d, args.split)
         ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
 
@@ -183,16 +233,18 @@ def main():
     avg_ms = sum(per) / len(per)
     ms_per_step = wall * 1e3 / args.steps
 
-    value = w.flops / (ms_per_step * 1e-3) / 1e12
-    achieved = w.flops / (avg_ms * 1e-3) / 1e12
+    flops = w.flops * (2.5 if args.bwd else 1.0)
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (avg_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
     log("[bench] %s: wall %.3f ms/step, kernel avg %.3f ms (min %.3f, max %.3f), "
         "%.1f TFLOP/s = %.1f%% of %.1f; %.0f GB/s algorithmic" % (
             w.name, ms_per_step, avg_ms, min(per), max(per), achieved,
             100 * achieved / peak, peak, w.algorithmic_bytes / (avg_ms * 1e-3) / 1e9))
 
+    kernel = "fa_bwd" if args.bwd else ("fa_fwd" if args.split == 1 else "fa_fwd_split")
     out = {
-        "metric": METRIC,
+        "metric": METRIC_BWD if args.bwd else METRIC,
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -204,15 +256,17 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic",
-        "config": dict(w.describe(), kernel="fa_fwd" if args.split == 1 else "fa_fwd_split",
-                       nsplit=args.split, parallelism="none (one GPU)"),
+        "config": dict(w.describe(), kernel=kernel, nsplit=args.split, parallelism="none (one GPU)"),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": traffic_record(w) if args.split == 1 else None},
+                     "traffic": traffic_record(w) if kernel == "fa_fwd" else None},
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on a sample (~%.0f s)" % args.cpu_budget)
-        out["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_budget)
+        if args.bwd:
+            out["cpu_baseline"] = cpu_baseline_bwd(w, q, k, v, args.cpu_budget)
+        else:
+            out["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_budget)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
