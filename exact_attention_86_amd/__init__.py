@@ -82,6 +82,9 @@ def lib() -> ctypes.CDLL:
         L.fa_bwd.restype = ctypes.c_int
         L.fa_bwd_workspace_bytes.argtypes = [i64, i64, i64]
         L.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
+        L.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float,
+                                 ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_int, vp]
+        L.fa_fwd_fp8.restype = ctypes.c_int
         _lib = L
         return L
 
@@ -138,6 +141,13 @@ def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, b, h, 
     return lib().fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, int(workspace_bytes),
                         int(b), int(h), int(sq), int(sk), int(d), float(scale), int(causal),
                         int(dtype), stream)
+
+
+def fa_fwd_fp8(q, k, v, o, lse, b, h, sq, sk, d, scale, descale_q, descale_k, descale_v, causal,
+               stream) -> int:
+    """The FP8 forward C entry point: device addresses as ints, returns the status code."""
+    return lib().fa_fwd_fp8(q, k, v, o, lse, int(b), int(h), int(sq), int(sk), int(d), float(scale),
+                            float(descale_q), float(descale_k), float(descale_v), int(causal), stream)
 
 
 def fa_bwd_workspace_bytes(b, h, sq) -> int:
@@ -271,3 +281,36 @@ def attention_bwd(q, k, v, out, lse, dout, causal: bool = False, scale: float | 
     if rc != FA_OK:
         raise FaError(rc, fa_last_error())
     return dq, dk, dv
+
+
+def attention_fp8(q, k, v, causal: bool = False, scale: float | None = None, descale_q: float = 1.0,
+                  descale_k: float = 1.0, descale_v: float = 1.0, out=None, lse=None, stream=None):
+    """O (bf16), LSE for E4M3 device tensors q [b,h,sq,d], k/v [b,h,sk,d]
+    (torch.float8_e4m3fn or their uint8 bytes) with per-tensor descale
+    factors.  Returns (O, LSE) without synchronising."""
+    import torch
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise FaError(FA_ERR_INVALID_ARG, "q, k, v must be 4-d [b, h, s, d]")
+    b, h, sq, d = q.shape
+    sk = k.shape[2]
+    if tuple(k.shape) != (b, h, sk, d) or tuple(v.shape) != (b, h, sk, d):
+        raise FaError(FA_ERR_INVALID_ARG, "k and v must be [b, h, sk, d] matching q")
+    for t in (q, k, v):
+        if not (t.is_cuda and t.is_contiguous()):
+            raise FaError(FA_ERR_INVALID_ARG, "q, k, v must be contiguous device tensors")
+        if t.dtype not in (torch.float8_e4m3fn, torch.uint8):
+            raise FaError(FA_ERR_UNSUPPORTED, "q, k, v must be float8_e4m3fn (or its uint8 bytes)")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((b, h, sq, d), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((b, h, sq), dtype=torch.float32, device=q.device)
+    s = stream if stream is not None else torch.cuda.current_stream(q.device)
+    rc = fa_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                    b, h, sq, sk, d, scale, descale_q, descale_k, descale_v, int(bool(causal)),
+                    s.cuda_stream)
+    if rc != FA_OK:
+        raise FaError(rc, fa_last_error())
+    return out, lse
+

@@ -34,7 +34,7 @@ extern "C" {
 
 FA_API const char* fa_last_error(void) { return g_err; }
 
-FA_API int fa_version(void) { return 400; /* 0.4.0: adds fa_bwd */ }
+FA_API int fa_version(void) { return 500; /* 0.5.0: adds fa_fwd_fp8 */ }
 
 FA_API int fa_query_config(int dtype, int64_t d, int causal, int64_t b, int64_t h, int64_t sq,
                            int64_t sk, int* block_m, int* block_n, int* waves, int* lds)
@@ -333,6 +333,55 @@ FA_API int fa_bwd(const void* q, const void* k, const void* v, const void* o, co
     hipError_t e = fa::launch_bwd(dtype, (int)d, p, (hipStream_t)stream);
     if (e != hipSuccess) {
         snprintf(g_err, sizeof g_err, "fa_bwd: launch failed: %s", hipGetErrorString(e));
+        return FA_ERR_HIP;
+    }
+    g_err[0] = 0;
+    return FA_OK;
+}
+
+FA_API int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int64_t b, int64_t h, int64_t sq, int64_t sk, int64_t d, float scale,
+                      float descale_q, float descale_k, float descale_v, int causal, void* stream)
+{
+    if (!q || !k || !v || !o || !lse) return fail(FA_ERR_INVALID_ARG, "fa_fwd_fp8: NULL pointer");
+    if (b <= 0 || h <= 0 || sq <= 0 || sk <= 0 || d <= 0)
+        return fail(FA_ERR_INVALID_ARG, "fa_fwd_fp8: b, h, sq, sk and d must be >= 1");
+    if (!isfinite(scale) || !isfinite(descale_q) || !isfinite(descale_k) || !isfinite(descale_v))
+        return fail(FA_ERR_INVALID_ARG, "fa_fwd_fp8: scale and descale factors must be finite");
+    if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARG, "fa_fwd_fp8: causal must be 0 or 1");
+    if (d != 128) return fail(FA_ERR_UNSUPPORTED, "fa_fwd_fp8: d = 128 only");
+    if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u)
+        return fail(FA_ERR_MISALIGNED, "fa_fwd_fp8: q, k, v, o must be 16-byte aligned");
+    if ((uintptr_t)lse & 3u) return fail(FA_ERR_MISALIGNED, "fa_fwd_fp8: lse must be 4-byte aligned");
+    const int64_t lim = INT32_MAX;
+    if (sq * d > lim || sk * d > lim || b * h > lim || b > lim || h > lim)
+        return fail(FA_ERR_TOO_LARGE, "fa_fwd_fp8: a per-head slice exceeds 2^31-1 elements");
+    const int64_t items = b * h * ((sq + 127) / 128);
+    if (items > lim - 8) return fail(FA_ERR_TOO_LARGE, "fa_fwd_fp8: too many tiles for one launch");
+    const size_t nq = (size_t)(b * h * sq * d), nk = (size_t)(b * h * sk * d);
+    const size_t no = nq * 2, nl = (size_t)(b * h * sq) * 4;
+    if (overlap(o, no, q, nq) || overlap(o, no, k, nk) || overlap(o, no, v, nk) ||
+        overlap(lse, nl, q, nq) || overlap(lse, nl, k, nk) || overlap(lse, nl, v, nk) ||
+        overlap(lse, nl, o, no))
+        return fail(FA_ERR_INVALID_ARG, "fa_fwd_fp8: o and lse must not overlap the inputs or each other");
+
+    fa::Fp8Params p;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.o = o;
+    p.lse = lse;
+    p.bh = (int)(b * h);
+    p.sq = (int)sq;
+    p.sk = (int)sk;
+    p.c = (float)((double)scale * (double)descale_q * (double)descale_k * 1.4426950408889634);
+    p.vscale = descale_v;
+    p.causal = causal;
+    p.items_per_head = 0;
+    p.n_items = 0;
+    hipError_t e = fa::launch_fwd_fp8(p, (hipStream_t)stream);
+    if (e != hipSuccess) {
+        snprintf(g_err, sizeof g_err, "fa_fwd_fp8: launch failed: %s", hipGetErrorString(e));
         return FA_ERR_HIP;
     }
     g_err[0] = 0;

@@ -58,20 +58,6 @@ __device__ __forceinline__ float widen16(uint32_t bits, bool bf16)
     return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
 }
 
-// workgroup id -> (head slice, work item), spreading consecutive ids over the
-// XCDs so each XCD takes a contiguous, head-major run of items (its L2 then
-// sees the same head's tensors from many workgroups)
-__device__ __forceinline__ bool map_bwd_item(int n_items, int items_per_head, int& bh, int& item)
-{
-    const int id = blockIdx.x;
-    const int per = (n_items + kXcds - 1) / kXcds;
-    const int t = (id % kXcds) * per + id / kXcds;
-    if (t >= n_items) return false;
-    bh = t / items_per_head;
-    item = t - bh * items_per_head;
-    return true;
-}
-
 // A operand of a 32x32x16 product from two 8-byte transpose reads at LDS
 // byte addresses a0 and a1
 __device__ __forceinline__ u32x4_t tr_pair(const char* a0, const char* a1)
@@ -136,7 +122,7 @@ fa_bwd_dkdv(BwdParams p)
     __shared__ __attribute__((aligned(16))) char lds[2 * STAGE];
 
     int bh, kt;
-    if (!map_bwd_item(p.n_items, p.items_per_head, bh, kt)) return;
+    if (!map_xcd_item(p.n_items, p.items_per_head, bh, kt)) return;
     const int tid = threadIdx.x;
     const int w = tid >> 6;
     const int lane = tid & 63;
@@ -369,7 +355,7 @@ fa_bwd_dq(BwdParams p)
     __shared__ __attribute__((aligned(16))) char lds[2 * STAGE];
 
     int bh, item;
-    if (!map_bwd_item(p.n_items, p.items_per_head, bh, item)) return;
+    if (!map_xcd_item(p.n_items, p.items_per_head, bh, item)) return;
     const int tid = threadIdx.x;
     const int w = tid >> 6;
     const int lane = tid & 63;

@@ -107,4 +107,19 @@ __device__ __forceinline__ void static_for(F&& f)
     }
 }
 
+// workgroup id -> (head slice, work item), spreading consecutive ids over the
+// XCDs so each XCD takes a contiguous, head-major run of items (its L2 then
+// sees the same head's tensors from many workgroups).  The grid is n_items
+// rounded up to a multiple of kXcds; ids past the last item return false.
+__device__ __forceinline__ bool map_xcd_item(int n_items, int items_per_head, int& bh, int& item)
+{
+    const int id = blockIdx.x;
+    const int per = (n_items + kXcds - 1) / kXcds;
+    const int t = (id % kXcds) * per + id / kXcds;
+    if (t >= n_items) return false;
+    bh = t / items_per_head;
+    item = t - bh * items_per_head;
+    return true;
+}
+
 }  // namespace fa

@@ -57,10 +57,27 @@ struct BwdParams {
     int n_items;
 };
 
+// FP8 forward launch parameters (fa_fwd_fp8).
+struct Fp8Params {
+    const void* q;       // E4M3 [bh][sq][128]
+    const void* k;       // E4M3 [bh][sk][128]
+    const void* v;       // E4M3 [bh][sk][128]
+    void* o;             // bf16 [bh][sq][128]
+    float* lse;          // fp32 [bh][sq]
+    int bh;
+    int sq, sk;
+    float c;             // scale * descale_q * descale_k * log2(e), signed
+    float vscale;        // descale_v
+    int causal;
+    int items_per_head;  // set by the launcher
+    int n_items;
+};
+
 bool tile_config(int dtype, int d, int64_t bh, int64_t sq, int causal, TileConfig* tc);
 hipError_t launch_fwd(int dtype, int d, const TileConfig& tc, const Params& p, hipStream_t stream);
 bool tile_config_split(int dtype, int d, TileConfig* tc);
 hipError_t launch_fwd_varlen(int dtype, int d, const Params& p, hipStream_t stream);
+hipError_t launch_fwd_fp8(const Fp8Params& p, hipStream_t stream);
 bool bwd_supported(int dtype, int d);
 hipError_t launch_bwd(int dtype, int d, const BwdParams& p, hipStream_t stream);
 hipError_t launch_fwd_split(int dtype, int d, const TileConfig& tc, const Params& p, hipStream_t stream);

@@ -220,6 +220,34 @@ FA_API int fa_bwd(const void* q, const void* k, const void* v, const void* o,
  * bytes; 0 for invalid arguments.  Host only. */
 FA_API size_t fa_bwd_workspace_bytes(int64_t b, int64_t h, int64_t sq);
 
+/*
+ * fa_fwd_fp8 -- the forward with FP8 inputs (page "05 · kernel 工程与四代演化",
+ * section 4.4, describes the FP8 forward and its exponent-range trick).
+ * Computes the attention of the dequantized tensors
+ *
+ *     O   = softmax(scale (descale_q Q)(descale_k K)^T) (descale_v V)
+ *     LSE = ln sum_j exp(scale descale_q descale_k q_i.k_j)
+ *
+ *   q          [b, h, sq, d] contiguous, OCP FP8 E4M3 (1 byte per element)
+ *   k, v       [b, h, sk, d] contiguous, E4M3
+ *   o          [b, h, sq, d] contiguous, bf16 (output)
+ *   lse        [b, h, sq] fp32 (output)
+ *   d          128
+ *   scale      finite; descale_q, descale_k, descale_v: finite per-tensor
+ *              factors that map the stored E4M3 values to the real ones
+ *   causal     0 or 1, as fa_fwd
+ *
+ * Both products run on FP8 matrix cores; the probabilities are rounded to
+ * E4M3 before the second product (the largest of a row is 2^8: the exponent
+ * reference is the row max minus 8), the row sum uses their fp32 values.
+ * Returns FA_OK or an fa_status code as fa_fwd (FA_ERR_UNSUPPORTED for
+ * d != 128).
+ */
+FA_API int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o,
+                      float* lse, int64_t b, int64_t h, int64_t sq, int64_t sk,
+                      int64_t d, float scale, float descale_q, float descale_k,
+                      float descale_v, int causal, void* stream);
+
 /* fa_last_error -- message of the last failing call on this host thread
  * ("" if none).  The pointer stays valid until the next call on the thread. */
 FA_API const char* fa_last_error(void);

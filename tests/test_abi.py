@@ -30,7 +30,8 @@ def declared_symbols():
 def test_header_declares_the_entry_points():
     assert set(declared_symbols()) == {"fa_fwd", "fa_fwd_split", "fa_split_workspace_bytes",
                                        "fa_fwd_varlen", "fa_query_config", "fa_last_error",
-                                       "fa_version", "fa_bwd", "fa_bwd_workspace_bytes"}
+                                       "fa_version", "fa_bwd", "fa_bwd_workspace_bytes",
+                                       "fa_fwd_fp8"}
 
 
 def test_library_loads_and_exports_every_declared_symbol():
@@ -41,7 +42,7 @@ def test_library_loads_and_exports_every_declared_symbol():
 
 
 def test_version():
-    assert fa.fa_version() >= 400
+    assert fa.fa_version() >= 500
 
 
 @pytest.mark.parametrize("dtype,d", [(fa.FA_F16, 64), (fa.FA_F16, 128), (fa.FA_F16, 256),
@@ -282,4 +283,41 @@ def test_bwd_binding_rejects_cpu_tensors():
     lse = torch.zeros(1, 1, 4)
     with pytest.raises(fa.FaError):
         fa.attention_bwd(x, x, x, x, lse, x)
+
+
+# ---- FP8 forward ----
+def call_fp8(**kw):
+    args = dict(q=Q, k=K, v=V, o=O, lse=L, b=1, h=2, sq=40, sk=50, d=128, scale=0.125,
+                descale_q=1.0, descale_k=1.0, descale_v=1.0, causal=0, stream=None)
+    args.update(kw)
+    return fa.fa_fwd_fp8(**args)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), fa.FA_ERR_INVALID_ARG),
+    (dict(lse=0), fa.FA_ERR_INVALID_ARG),
+    (dict(sq=0), fa.FA_ERR_INVALID_ARG),
+    (dict(sk=0), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), fa.FA_ERR_INVALID_ARG),
+    (dict(descale_q=float("nan")), fa.FA_ERR_INVALID_ARG),
+    (dict(descale_v=float("inf")), fa.FA_ERR_INVALID_ARG),
+    (dict(causal=5), fa.FA_ERR_INVALID_ARG),
+    (dict(d=64), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=256), fa.FA_ERR_UNSUPPORTED),
+    (dict(v=V + 8), fa.FA_ERR_MISALIGNED),
+    (dict(lse=L + 2), fa.FA_ERR_MISALIGNED),
+    (dict(o=K + 16), fa.FA_ERR_INVALID_ARG),       # o over k
+    (dict(lse=O + 64), fa.FA_ERR_INVALID_ARG),     # lse inside o (o is 2 bytes per element)
+    (dict(sq=1 << 24), fa.FA_ERR_TOO_LARGE),
+])
+def test_fp8_invalid_arguments_rejected_before_launch(kw, code):
+    assert call_fp8(**kw) == code
+    assert fa.fa_last_error().startswith("fa_fwd_fp8")
+
+
+def test_fp8_binding_rejects_wrong_dtype():
+    import torch
+    x = torch.zeros(1, 1, 4, 128, dtype=torch.bfloat16)
+    with pytest.raises(fa.FaError):
+        fa.attention_fp8(x, x, x)
 

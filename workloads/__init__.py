@@ -134,3 +134,23 @@ def make_dout(w: Workload, seed: int | None = None):
     g = rng.standard_normal((w.b, w.h, w.sq, w.d), dtype=np.float64).astype(np.float32)
     return torch.from_numpy(g).to(_torch_dtype(w.dtype))
 
+
+FP8_MAX = 448.0  # largest finite OCP E4M3 value
+
+
+def make_fp8(w: Workload, seed: int | None = None):
+    """FP8 inputs for the same draws as ``make``: each of Q, K, V (fp32) is
+    multiplied by a power of two that brings its largest magnitude into
+    (FP8_MAX/2, FP8_MAX], rounded to OCP E4M3 (torch, round to nearest even),
+    and paired with the inverse power of two as its descale factor.  Returns
+    (q8, k8, v8, (descale_q, descale_k, descale_v)) with CPU tensors of dtype
+    torch.float8_e4m3fn; dequantized value = stored E4M3 value * descale."""
+    import torch
+    out, desc = [], []
+    for a in draw_f32(w, seed):
+        amax = float(np.max(np.abs(a))) if a.size else 1.0
+        e = math.floor(math.log2(FP8_MAX / amax)) if amax > 0 else 0
+        out.append(torch.from_numpy(a * np.float32(2.0 ** e)).to(torch.float8_e4m3fn))
+        desc.append(2.0 ** -e)
+    return out[0], out[1], out[2], tuple(desc)
+
