@@ -1,7 +1,7 @@
 """Throughput of the exact-attention prefill forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--split N | --bwd] [--no-cpu-baseline]
+                    [--split N | --bwd | --fp8] [--no-cpu-baseline]
 
 One step is one fa_fwd call (the whole hot path: tile schedule, Q/K/V tile
 loads, S = QK^T, masking, online softmax, O += PV, epilogue) over the
@@ -12,6 +12,10 @@ is one fa_bwd call (the D = dO.O pass, the dK/dV kernel and the dQ kernel)
 on O and LSE that one fa_fwd call produced before timing; its FLOP count is
 the usual 2.5x the forward's (five sq x sk x d products where the forward has
 two), and the roofline covers the three kernels of the call together.
+With --fp8 a step is one fa_fwd_fp8 call on the workload's draws quantized to
+OCP E4M3 with per-tensor power-of-two descale factors; its roofline is priced
+against the dense FP8 matrix peak and its oracle leg runs on the dequantized
+values.
 Warm-up runs at least W steps and at least 0.5 s of launches (clocks settle).
 Prints ONE JSON line.  ``value`` is TFLOP/s with the usual attention count
 4*b*h*sq*sk*d (halved when causal) over the wall-clock of the K timed steps;
@@ -39,9 +43,10 @@ import numpy as np  # noqa: E402
 import workloads as W  # noqa: E402
 
 METRIC = "attn fwd TFLOP/s, b4 h32 sq4096 d128 bf16 causal; % of MFMA peak"
+METRIC_FP8 = "attn fwd TFLOP/s, b4 h32 sq4096 d128 fp8 e4m3 inputs (bf16 out) causal; % of FP8 MFMA peak"
 METRIC_BWD = "attn bwd TFLOP/s (2.5x fwd FLOP count), b4 h32 sq4096 d128 bf16 causal; % of MFMA peak"
 # MI355X dense matrix peaks (TFLOP/s): 256 CUs x 2.4 GHz x FLOP/clk/CU
-PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}
+PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3, "fp8_e4m3": 5033.2}
 PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_86_amd", "csrc", f)
                   for f in ("fa_fwd_kernels.hip", "fa_device.h", "fa_kernels.h", "fa_api.cpp")]
@@ -134,6 +139,8 @@ def main():
                     help="split-KV parts per query tile (fa_fwd_split); 1 = fa_fwd")
     ap.add_argument("--bwd", action="store_true",
                     help="time the backward (fa_bwd) instead of the forward")
+    ap.add_argument("--fp8", action="store_true",
+                    help="time the FP8 forward (fa_fwd_fp8) on E4M3-quantized inputs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -167,6 +174,15 @@ def main():
     q, k, v = W.make(w)
     qd, kd, vd = (t.to(dev) for t in (q, k, v))
     od = torch.empty_like(qd)
+    if args.fp8:
+        if args.bwd or args.split > 1 or w.dtype == "f32":
+            print("--fp8 runs the forward of a 16-bit workload only", file=sys.stderr)
+            sys.exit(2)
+        q8, k8, v8, desc = W.make_fp8(w)
+        # the oracle leg sees the dequantized values the kernel computes on
+        q, k, v = (t.to(torch.float64).numpy() * s for t, s in zip((q8, k8, v8), desc))
+        qd, kd, vd = (t.to(dev) for t in (q8, k8, v8))
+        od = torch.empty((w.b, w.h, w.sq, w.d), dtype=torch.bfloat16, device=dev)
     lsed = torch.empty((w.b, w.h, w.sq), dtype=torch.float32, device=dev)
     scale = float(np.float32(w.scale))
     stream = torch.cuda.current_stream(dev)
@@ -199,6 +215,12 @@ def main():
         def step():
             rc = fa.fa_fwd_split(*ptrs, w.b, w.h, w.sq, w.sk, w.d, scale, int(w.causal), code,
                                  args.split, ws.data_ptr(), ws_bytes, stream.cuda_stream)
+            if rc != fa.FA_OK:
+                raise fa.FaError(rc, fa.fa_last_error())
+    elif args.fp8:
+        def step():
+            rc = fa.fa_fwd_fp8(*ptrs, w.b, w.h, w.sq, w.sk, w.d, scale, desc[0], desc[1], desc[2],
+                               int(w.causal), stream.cuda_stream)
             if rc != fa.FA_OK:
                 raise fa.FaError(rc, fa.fa_last_error())
     else:
@@ -236,15 +258,17 @@ def main():
     flops = w.flops * (2.5 if args.bwd else 1.0)
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (avg_ms * 1e-3) / 1e12
-    peak = PEAK_TFLOPS[w.dtype]
+    dtype = "fp8_e4m3" if args.fp8 else w.dtype
+    peak = PEAK_TFLOPS[dtype]
     log("[bench] %s: wall %.3f ms/step, kernel avg %.3f ms (min %.3f, max %.3f), "
         "%.1f TFLOP/s = %.1f%% of %.1f; %.0f GB/s algorithmic" % (
             w.name, ms_per_step, avg_ms, min(per), max(per), achieved,
             100 * achieved / peak, peak, w.algorithmic_bytes / (avg_ms * 1e-3) / 1e9))
 
-    kernel = "fa_bwd" if args.bwd else ("fa_fwd" if args.split == 1 else "fa_fwd_split")
+    kernel = "fa_bwd" if args.bwd else ("fa_fwd_fp8" if args.fp8 else
+                                         ("fa_fwd" if args.split == 1 else "fa_fwd_split"))
     out = {
-        "metric": METRIC_BWD if args.bwd else METRIC,
+        "metric": METRIC_BWD if args.bwd else (METRIC_FP8 if args.fp8 else METRIC),
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -254,7 +278,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": w.dtype,
+        "dtype": dtype,
         "data": "synthetic",
         "config": dict(w.describe(), kernel=kernel, nsplit=args.split, parallelism="none (one GPU)"),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,

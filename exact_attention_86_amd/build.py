@@ -27,8 +27,8 @@ def hip_flags():
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every source and link libfa.so; returns its path."""
-    objs = []
+    """Compile every source (in parallel) and link libfa.so; returns its path."""
+    objs, procs = [], []
     for src in SOURCES:
         path = os.path.join(CSRC, src)
         obj = os.path.join(CSRC, src + ".o")
@@ -36,14 +36,19 @@ def build(verbose: bool = False) -> str:
         cmd = [HIPCC] + hip_flags() + lang + ["-c", path, "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
-        r = subprocess.run(cmd, capture_output=True, text=True)
-        errs = [ln for ln in (r.stderr or "").splitlines()
-                if "packed-fp32-ops" not in ln]
-        if r.returncode != 0:
-            raise RuntimeError("hipcc failed on %s:\n%s" % (src, "\n".join(errs)))
-        if verbose and errs:
-            print("\n".join(errs), file=sys.stderr)
+        procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE,
+                                            stderr=subprocess.PIPE, text=True)))
         objs.append(obj)
+    failed = []
+    for src, p in procs:
+        _, err = p.communicate()
+        errs = [ln for ln in (err or "").splitlines() if "packed-fp32-ops" not in ln]
+        if p.returncode != 0:
+            failed.append("hipcc failed on %s:\n%s" % (src, "\n".join(errs)))
+        elif verbose and errs:
+            print("\n".join(errs), file=sys.stderr)
+    if failed:
+        raise RuntimeError("\n".join(failed))
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC"] + objs + ["-o", tmp]
     if verbose:
