@@ -21,9 +21,15 @@
 // blocks); the A operand V^T must list the same keys in the same byte slots,
 // which 8-byte transpose reads (ds_read_b64_tr_b8: lane s of a 16-lane group
 // receives byte s%8 of the 8 bytes each of lanes 2b + s/8 addressed, for
-// b = 0..7) deliver from V rows in LDS.  The exact row max is taken every
-// tile, as the page's recurrence does, so no probability exceeds 2^8 (E4M3
-// holds up to 448).
+// b = 0..7) deliver from V rows in LDS.  The exact tile max is taken every
+// tile, but the exponent reference (the running max) is raised -- with the
+// rescale of O and the row sum -- only when a row's tile max exceeds it by
+// more than 0.75 in log2 units: any reference gives the same result up to
+// rounding, no probability exceeds 2^8.75 < 448 (E4M3's largest value), the
+// row max still contributes at least 2^8 to the row sum, and the O rescale
+// becomes rare once the running maxima settle.  A negative exponent factor
+// enters as Q with its sign bits flipped, so the tile max of the raw scores
+// is the tile max of the exponents.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -91,7 +97,11 @@ fa_fwd_fp8(Fp8Params p)
     const int l32 = lane & 31;
     const int g = lane >> 5;
     const int sq = p.sq, sk = p.sk;
-    const float c = p.c;  // scale * dq * dk * log2(e)
+    // |scale * dq * dk| * log2(e); a zero factor becomes 1e-30, which leaves
+    // exp2 of every score at exactly 2^8 and keeps masked scores at -inf
+    const float c = fmaxf(fabsf(p.c), 1e-30f);
+    const int qsign = p.c < 0.f ? (int)0x80808080u : 0;  // negative factor: Q enters negated
+    constexpr float kSlack = 0.75f;                      // log2 units: 2^(8 + 0.75) < 448
     const int mt = CAUSAL ? p.items_per_head - 1 - item : item;  // causal: heaviest tiles first
     const int q0 = mt * BM;
 
@@ -108,8 +118,8 @@ fa_fwd_fp8(Fp8Params p)
     i32x8_t qf[2];
     {
         const uint8_t* qp = Q + (size_t)min(qrow, sq - 1) * D + 32 * g;
-        qf[0] = *(const i32x8_t*)(qp);
-        qf[1] = *(const i32x8_t*)(qp + 64);
+        qf[0] = *(const i32x8_t*)(qp) ^ qsign;
+        qf[1] = *(const i32x8_t*)(qp + 64) ^ qsign;
     }
 
     const int q_end = min(q0 + BM, sq);
@@ -195,36 +205,40 @@ fa_fwd_fp8(Fp8Params p)
             }
         }
 
-        // ---- scores in log2 units, masks (ragged keys, causal diagonal) ----
+        // ---- masks (ragged keys, causal diagonal) on the raw scores, tile max ----
         const bool need_mask = (n0 + BN > sk) || (CAUSAL && n0 + BN - 1 > wq);
-        float mx = -INFINITY;
+        if (need_mask) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = n0 + kb * 32 + (r >> 2) * 8 + 4 * g + (r & 3);
+                    if (key >= sk || (CAUSAL && key > qrow)) s[kb][r] = -INFINITY;
+                }
+        }
+        float mx = s[0][0];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float x = s[kb][r] * c;
-                if (need_mask) {
-                    const int key = n0 + kb * 32 + (r >> 2) * 8 + 4 * g + (r & 3);
-                    if (key >= sk || (CAUSAL && key > qrow)) x = -INFINITY;
-                }
-                s[kb][r] = x;
-                mx = fmaxf(mx, x);
-            }
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
         mx = fmaxf(mx, __shfl_xor(mx, 32));  // lanes l and l+32 share a query
+        const float mt = mx * c;
 
-        // ---- online softmax with the exact max; the exponent reference is the
-        //      max minus 8, so probabilities lie in [0, 2^8] ----
-        const float m_new = fmaxf(m_run, mx);
-        if (__builtin_amdgcn_ballot_w64(m_new > m_run)) {
-            const float alpha = fast_exp2(m_run - m_new);  // 0 when m_run = -inf
+        // ---- online softmax: the reference m_run is raised to the exact
+        //      running max only when a tile max exceeds it by more than kSlack;
+        //      the exponent reference is m_run - 8, so probabilities lie in
+        //      [0, 2^(8 + kSlack)] ----
+        if (__builtin_amdgcn_ballot_w64(mt > m_run + kSlack)) {
+            const float m_new = fmaxf(m_run, mt);
+            const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m_new);
             l_run *= alpha;
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+            m_run = m_new;
         }
-        m_run = m_new;
-        const float ref = m_new - 8.f;
+        const float ref = m_run - 8.f;
         // B operand: byte slot i holds the probability of key block i/16, score
         // register i%16
         i32x8_t pb;
@@ -232,10 +246,10 @@ fa_fwd_fp8(Fp8Params p)
 #pragma unroll
         for (int q4 = 0; q4 < 8; ++q4) {
             const int kb = q4 >> 2, r0 = (q4 & 3) * 4;
-            const float p0 = fast_exp2(s[kb][r0] - ref);
-            const float p1 = fast_exp2(s[kb][r0 + 1] - ref);
-            const float p2 = fast_exp2(s[kb][r0 + 2] - ref);
-            const float p3 = fast_exp2(s[kb][r0 + 3] - ref);
+            const float p0 = fast_exp2(__builtin_fmaf(s[kb][r0], c, -ref));
+            const float p1 = fast_exp2(__builtin_fmaf(s[kb][r0 + 1], c, -ref));
+            const float p2 = fast_exp2(__builtin_fmaf(s[kb][r0 + 2], c, -ref));
+            const float p3 = fast_exp2(__builtin_fmaf(s[kb][r0 + 3], c, -ref));
             acc += (p0 + p1) + (p2 + p3);
             pb[q4] = pack4_fp8(p0, p1, p2, p3);
         }

@@ -238,8 +238,11 @@ FA_API size_t fa_bwd_workspace_bytes(int64_t b, int64_t h, int64_t sq);
  *   causal     0 or 1, as fa_fwd
  *
  * Both products run on FP8 matrix cores; the probabilities are rounded to
- * E4M3 before the second product (the largest of a row is 2^8: the exponent
- * reference is the row max minus 8), the row sum uses their fp32 values.
+ * E4M3 before the second product, the row sum uses their fp32 values.  The
+ * exponent reference is a running reference max minus 8, where the reference
+ * never exceeds the row max seen so far and trails it by at most 0.75 (log2
+ * units): the row max contributes at least 2^8 to the row sum and no
+ * probability exceeds 2^8.75 (E4M3's largest value is 448).
  * Returns FA_OK or an fa_status code as fa_fwd (FA_ERR_UNSUPPORTED for
  * d != 128).
  */

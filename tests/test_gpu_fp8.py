@@ -82,6 +82,8 @@ CASES = [
     (2, 2, 640, 384, False, 0.2),
     (1, 2, 190, 140, False, -0.07),
     (2, 4, 1024, 1024, True, None),
+    (1, 2, 150, 150, True, 0.0),     # uniform weights over each causal prefix
+    (1, 2, 256, 512, False, 1.0),    # near one-hot rows: the reference max moves often
 ]
 
 
