@@ -95,6 +95,23 @@ def test_fp8_matches_oracle(case):
     check_fp8(w)
 
 
+# many heads (grids of 256-1024 workgroups), ragged query and key tails,
+# sq != sk, causal and not
+MANY_HEAD_CASES = [
+    (1, 256, 300, 300, True, None),
+    (2, 128, 260, 260, False, None),
+    (1, 256, 200, 333, True, None),
+]
+
+
+@pytest.mark.parametrize("case", MANY_HEAD_CASES, ids=lambda c: "b%dh%d_sq%d_sk%d_%s" % (
+    c[0], c[1], c[2], c[3], "causal" if c[4] else "full"))
+def test_fp8_many_heads(case):
+    b, h, sq, sk, causal, scale = case
+    w = W.shape("fp8heads", "bf16", b, h, sq, sk, 128, causal, scale=scale, seed=7 * sq + sk)
+    check_fp8(w)
+
+
 def test_fp8_headline_shape_sampled_rows():
     """The [4, 32, 4096, 128] causal problem at full size; the oracle computes
     sampled rows (first and last tiles of two heads, tile edges, random)."""
