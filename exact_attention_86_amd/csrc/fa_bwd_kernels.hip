@@ -249,6 +249,19 @@ fa_bwd_dkdv(BwdParams p)
                 dp = mfma16(ag, vf[kk], dp, BF16);
             }
 
+            // ---- the transposed dO and Q operands of the dV and dK products
+            //      go out now, so their LDS latency hides behind the softmax ----
+            u32x4_t opg[2][NDT], opq[2][NDT];
+#pragma unroll
+            for (int kc = 0; kc < 2; ++kc) {
+                const char* base = qblk + kc * 16 * RB;
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt) {
+                    opg[kc][dt] = tr_pair(base + TQ + rt[0][dt], base + TQ + rt[1][dt]);
+                    opq[kc][dt] = tr_pair(base + rt[0][dt], base + rt[1][dt]);
+                }
+            }
+
             // ---- P = exp2(c s - LSE log2 e), dS = P (dP - D); accumulator row
             //      r holds query 8(r/4) + 4g + r%4 of the block ----
             f32x4_t l4[4], d4[4];
@@ -279,16 +292,12 @@ fa_bwd_dkdv(BwdParams p)
 
             // ---- dV^T += dO^T P and dK^T += Q^T dS over this block's queries ----
 #pragma unroll
-            for (int kc = 0; kc < 2; ++kc) {
-                const char* base = qblk + kc * 16 * RB;
+            for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
                 for (int dt = 0; dt < NDT; ++dt) {
-                    const u32x4_t ag = tr_pair(base + TQ + rt[0][dt], base + TQ + rt[1][dt]);
-                    dva[dt] = mfma16(ag, pp[kc], dva[dt], BF16);
-                    const u32x4_t aq = tr_pair(base + rt[0][dt], base + rt[1][dt]);
-                    dka[dt] = mfma16(aq, dsp[kc], dka[dt], BF16);
+                    dva[dt] = mfma16(opg[kc][dt], pp[kc], dva[dt], BF16);
+                    dka[dt] = mfma16(opq[kc][dt], dsp[kc], dka[dt], BF16);
                 }
-            }
         }
     };
 
