@@ -266,6 +266,13 @@ def test_split_kv_full_compare(case, gpu):
     compare_full(W.shape("split", dt, b, h, sq, sk, d, causal, seed=sq + 3 * sk), nsplit=nsplit)
 
 
+@pytest.mark.parametrize("nsplit", [1, 64])
+def test_million_keys(nsplit, gpu):
+    """16 queries against 2^20 keys: the row sum and O accumulate in fp32
+    over 16384 key tiles (one workgroup per head without splitting)."""
+    compare_full(W.shape("longkeys", "bf16", 1, 2, 16, 1 << 20, 128, False, seed=11), nsplit=nsplit)
+
+
 def test_split_one_part_is_fa_fwd(gpu):
     import torch
     w = W.shape("split1", "bf16", 1, 2, 200, 333, 128, True, seed=11)
