@@ -348,6 +348,8 @@ FA_API int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, floa
         return fail(FA_ERR_INVALID_ARG, "fa_fwd_fp8: b, h, sq, sk and d must be >= 1");
     if (!isfinite(scale) || !isfinite(descale_q) || !isfinite(descale_k) || !isfinite(descale_v))
         return fail(FA_ERR_INVALID_ARG, "fa_fwd_fp8: scale and descale factors must be finite");
+    if (!isfinite((float)((double)scale * (double)descale_q * (double)descale_k * 1.4426950408889634)))
+        return fail(FA_ERR_INVALID_ARG, "fa_fwd_fp8: scale * descale_q * descale_k overflows fp32");
     if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARG, "fa_fwd_fp8: causal must be 0 or 1");
     if (d != 128) return fail(FA_ERR_UNSUPPORTED, "fa_fwd_fp8: d = 128 only");
     if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u)

@@ -234,7 +234,8 @@ FA_API size_t fa_bwd_workspace_bytes(int64_t b, int64_t h, int64_t sq);
  *   lse        [b, h, sq] fp32 (output)
  *   d          128
  *   scale      finite; descale_q, descale_k, descale_v: finite per-tensor
- *              factors that map the stored E4M3 values to the real ones
+ *              factors that map the stored E4M3 values to the real ones;
+ *              scale * descale_q * descale_k * log2(e) must be finite in fp32
  *   causal     0 or 1, as fa_fwd
  *
  * Both products run on FP8 matrix cores; the probabilities are rounded to

@@ -301,6 +301,7 @@ def call_fp8(**kw):
     (dict(scale=float("inf")), fa.FA_ERR_INVALID_ARG),
     (dict(descale_q=float("nan")), fa.FA_ERR_INVALID_ARG),
     (dict(descale_v=float("inf")), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=1e30, descale_q=1e30), fa.FA_ERR_INVALID_ARG),  # finite factors, product overflows
     (dict(causal=5), fa.FA_ERR_INVALID_ARG),
     (dict(d=64), fa.FA_ERR_UNSUPPORTED),
     (dict(d=256), fa.FA_ERR_UNSUPPORTED),
