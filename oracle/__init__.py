@@ -27,6 +27,8 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "attn_oracle.c")
+# deliberately broken copies for the pin tests, kept apart from the definition
+_SRC_MUTANTS = os.path.join(_HERE, "attn_mutants.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lock = threading.Lock()
 _lib = None
@@ -56,11 +58,11 @@ BWD_MUTANTS = {
 def build(force: bool = True) -> str:
     """Compile attn_oracle.c into liboracle.so with gcc; returns the path."""
     if not force and os.path.exists(_LIB_PATH) and \
-            os.path.getmtime(_LIB_PATH) >= os.path.getmtime(_SRC):
+            os.path.getmtime(_LIB_PATH) >= max(os.path.getmtime(_SRC), os.path.getmtime(_SRC_MUTANTS)):
         return _LIB_PATH
     tmp = _LIB_PATH + ".tmp%d" % os.getpid()
     cmd = ["gcc", "-O3", "-std=c11", "-march=x86-64-v2", "-fPIC", "-shared",
-           "-pthread", _SRC, "-o", tmp, "-lm"]
+           "-pthread", _SRC, _SRC_MUTANTS, "-o", tmp, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
@@ -83,10 +85,11 @@ def _load():
         lib.oracle_attn_probs.argtypes = [dp, dp, dp, dp, dp, dp] + dims
         lib.oracle_attn_online_kv_outer.argtypes = [dp, dp, dp, dp, dp] + dims + [i64, i64]
         lib.oracle_attn_online_q_outer.argtypes = [dp, dp, dp, dp, dp] + dims + [i64, i64]
-        lib.oracle_attn_bwd.argtypes = [dp, dp, dp, dp, dp, dp, dp] + dims + [ctypes.c_int, ctypes.c_int]
+        lib.oracle_attn_bwd.argtypes = [dp, dp, dp, dp, dp, dp, dp] + dims + [ctypes.c_int]
+        lib.oracle_attn_bwd_mutant.argtypes = [dp, dp, dp, dp, dp, dp, dp] + dims + [ctypes.c_int]
         for f in ("oracle_attn", "oracle_attn_mutant", "oracle_attn_rows",
                   "oracle_attn_probs", "oracle_attn_online_kv_outer",
-                  "oracle_attn_online_q_outer", "oracle_attn_bwd"):
+                  "oracle_attn_online_q_outer", "oracle_attn_bwd", "oracle_attn_bwd_mutant"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
         return lib
@@ -142,7 +145,8 @@ def attn(q, k, v, scale, causal=False, nthreads=None):
 
 
 def attn_mutant(q, k, v, scale, causal, mutant, nthreads=None):
-    """The definition with one deliberate mistake (see MUTANTS); pin tests only."""
+    """A deliberately broken copy of the definition (see MUTANTS; the copy
+    lives in attn_mutants.c, apart from the definition); pin tests only."""
     q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
     b, h, sq, sk, d = _shapes(q, k, v)
     o = np.empty((b, h, sq, d), np.float64)
@@ -219,7 +223,8 @@ def attn_online_q_outer(q, k, v, scale, causal=False, br=64, bc=64):
 def attn_bwd(q, k, v, dout, scale, causal=False, mutant=0, nthreads=None):
     """Gradient of the definition: (dQ, dK, dV) of sum(O * dout), fp64.
 
-    ``mutant`` selects a deliberate mistake (BWD_MUTANTS); pin tests only."""
+    ``mutant`` != 0 runs a deliberately broken copy instead (BWD_MUTANTS; the
+    copy lives in attn_mutants.c); pin tests only."""
     q, k, v, g = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(dout)
     b, h, sq, sk, d = _shapes(q, k, v)
     if g.shape != q.shape:
@@ -228,9 +233,14 @@ def attn_bwd(q, k, v, dout, scale, causal=False, mutant=0, nthreads=None):
     dk = np.empty_like(k)
     dv = np.empty_like(v)
     code = BWD_MUTANTS[mutant] if isinstance(mutant, str) else int(mutant)
-    rc = _load().oracle_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(dq), _ptr(dk), _ptr(dv),
-                                 b, h, sq, sk, d, _scale_f64(scale), int(bool(causal)), code,
-                                 int(nthreads or default_threads()))
+    if code:
+        rc = _load().oracle_attn_bwd_mutant(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(dq), _ptr(dk),
+                                            _ptr(dv), b, h, sq, sk, d, _scale_f64(scale),
+                                            int(bool(causal)), code)
+    else:
+        rc = _load().oracle_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(dq), _ptr(dk), _ptr(dv),
+                                     b, h, sq, sk, d, _scale_f64(scale), int(bool(causal)),
+                                     int(nthreads or default_threads()))
     if rc:
         raise ValueError("oracle_attn_bwd rejected its arguments")
     return dq, dk, dv

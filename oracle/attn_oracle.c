@@ -39,14 +39,13 @@
  *                           and an unnormalised accumulator divided by l at
  *                           the end (the order the FA2 traits described on
  *                           page "05 · kernel 工程与四代演化" section 3 use).
- *   oracle_attn_mutant   -- the naive definition with one deliberate,
- *                           selectable mistake; the pin tests use it to show
- *                           each plausible mistake fails at least one pin.
  *   oracle_attn_bwd      -- the gradient of the definition: given dO, the
  *                           derivatives dQ, dK, dV of sum(O * dO) (the pages
  *                           name a backward kernel class but print no formula;
- *                           this is the calculus of the forward definition),
- *                           with an optional deliberate mistake for the pins.
+ *                           this is the calculus of the forward definition).
+ *
+ * The deliberately broken copies the pin tests use to show that every pin
+ * bites live in attn_mutants.c, apart from the definition above.
  *
  * All arrays are fp64, contiguous, row-major: q,o [b,h,sq,d]; k,v [b,h,sk,d];
  * lse [b,h,sq].  Return value 0 on success, -1 on invalid arguments.
@@ -63,31 +62,12 @@
 /* The plain definition for one query row.                                   */
 /* ------------------------------------------------------------------------ */
 
-/* mutant codes (0 = the correct definition) */
-enum {
-    MUT_NONE = 0,
-    MUT_NO_SCALE = 1,        /* scale never applied to the dot product     */
-    MUT_CAUSAL_STRICT = 2,   /* causal mask j < i instead of j <= i        */
-    MUT_K_TRANSPOSED = 3,    /* reads K as if stored [d, sk]               */
-    MUT_LSE_NO_MAX = 4,      /* LSE forgets to add the row max back        */
-    MUT_NO_NORMALISE = 5,    /* O is not divided by the row sum l          */
-    MUT_DROP_LAST_KEY = 6,   /* loop bound sk-1 instead of sk              */
-    MUT_EXP_SIGN = 7,        /* exp(m - s) instead of exp(s - m)           */
-    MUT_V_ROW_OFF = 8,       /* weights key j's probability onto V row j+1 */
-    MUT_MAX_LAST = 9         /* uses the last score instead of the max;
-                                harmless in exact arithmetic, so this one
-                                is caught only by overflow (a range pin)   */
-};
-
-static inline int64_t key_limit(int64_t i, int64_t sk, int causal, int mut)
+/* number of keys row i may attend to: keys 0 .. limit-1 (all sk keys, or
+ * with the causal mask the keys j <= i) */
+static inline int64_t key_limit(int64_t i, int64_t sk, int causal)
 {
-    /* number of keys row i may attend to: keys 0 .. limit-1 */
     int64_t lim = sk;
-    if (causal) {
-        int64_t c = (mut == MUT_CAUSAL_STRICT) ? i : i + 1;
-        if (c < lim) lim = c;
-    }
-    if (mut == MUT_DROP_LAST_KEY && lim > 1) lim -= 1;
+    if (causal && i + 1 < lim) lim = i + 1;
     return lim;
 }
 
@@ -112,58 +92,38 @@ static double dot(const double* a, const double* b, int64_t d)
  * (zero for keys the row may not attend to). */
 static double attend_row(const double* qi, const double* kh, const double* vh,
                          int64_t i, int64_t sk, int64_t d, double scale,
-                         int causal, int mut, double* s, double* oi,
-                         double* p_out)
+                         int causal, double* s, double* oi, double* p_out)
 {
-    const int64_t n = key_limit(i, sk, causal, mut);
+    const int64_t n = key_limit(i, sk, causal);
 
     /* scores s_j = scale * (q_i . k_j) */
-    for (int64_t j = 0; j < n; ++j) {
-        double dp;
-        if (mut == MUT_K_TRANSPOSED) {
-            /* K read as a [d, sk] matrix: element (j, x) at x*sk + j */
-            dp = 0.0;
-            for (int64_t x = 0; x < d; ++x) dp += qi[x] * kh[x * sk + j];
-        } else {
-            dp = dot(qi, kh + j * d, d);
-        }
-        s[j] = (mut == MUT_NO_SCALE) ? dp : scale * dp;
-    }
+    for (int64_t j = 0; j < n; ++j) s[j] = scale * dot(qi, kh + j * d, d);
 
-    /* row max */
+    /* row max m */
     double m = -INFINITY;
-    if (mut == MUT_MAX_LAST) {
-        m = (n > 0) ? s[n - 1] : -INFINITY;
-    } else {
-        for (int64_t j = 0; j < n; ++j)
-            if (s[j] > m) m = s[j];
-    }
+    for (int64_t j = 0; j < n; ++j)
+        if (s[j] > m) m = s[j];
 
     /* p_j = exp(s_j - m), l = sum_j p_j */
     double l = 0.0;
     for (int64_t j = 0; j < n; ++j) {
-        s[j] = (mut == MUT_EXP_SIGN) ? exp(m - s[j]) : exp(s[j] - m);
+        s[j] = exp(s[j] - m);
         l += s[j];
     }
 
     /* o = sum_j p_j v_j / l */
     for (int64_t x = 0; x < d; ++x) oi[x] = 0.0;
     for (int64_t j = 0; j < n; ++j) {
-        int64_t row = j;
-        if (mut == MUT_V_ROW_OFF) row = (j + 1 < sk) ? j + 1 : j;
-        const double* vj = vh + row * d;
-        const double p = s[j];
-        for (int64_t x = 0; x < d; ++x) oi[x] += p * vj[x];
+        const double* vj = vh + j * d;
+        for (int64_t x = 0; x < d; ++x) oi[x] += s[j] * vj[x];
     }
-    if (mut != MUT_NO_NORMALISE) {
-        const double inv = 1.0 / l;
-        for (int64_t x = 0; x < d; ++x) oi[x] *= inv;
-    }
+    for (int64_t x = 0; x < d; ++x) oi[x] /= l;
 
-    if (p_out) {
+    if (p_out)
         for (int64_t j = 0; j < sk; ++j) p_out[j] = (j < n) ? s[j] / l : 0.0;
-    }
-    return (mut == MUT_LSE_NO_MAX) ? log(l) : m + log(l);
+
+    /* LSE = m + ln l */
+    return m + log(l);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -175,7 +135,7 @@ typedef struct {
     double *o, *lse, *p;
     int64_t bh, sq, sk, d;
     double scale;
-    int causal, mut;
+    int causal;
     const int64_t* rows; /* optional row list (flat index bh_idx*sq + i) */
     int64_t nrows;
     int tid, nthreads;
@@ -204,7 +164,7 @@ static void* run_rows(void* arg)
             double* oi = J->o + r * J->d;
             double* pi = J->p ? J->p + r * J->sk : NULL;
             const double l = attend_row(qi, kh, vh, i, J->sk, J->d, J->scale,
-                                        J->causal, J->mut, s, oi, pi);
+                                        J->causal, s, oi, pi);
             J->lse[r] = l;
         }
     }
@@ -247,26 +207,17 @@ static int bad_dims(int64_t b, int64_t h, int64_t sq, int64_t sk, int64_t d)
 /* Public entry points                                                       */
 /* ------------------------------------------------------------------------ */
 
-int oracle_attn_mutant(const double* q, const double* k, const double* v,
-                       double* o, double* lse, int64_t b, int64_t h,
-                       int64_t sq, int64_t sk, int64_t d, double scale,
-                       int causal, int mutant, int nthreads)
+int oracle_attn(const double* q, const double* k, const double* v, double* o,
+                double* lse, int64_t b, int64_t h, int64_t sq, int64_t sk,
+                int64_t d, double scale, int causal, int nthreads)
 {
     if (!q || !k || !v || !o || !lse || bad_dims(b, h, sq, sk, d)) return -1;
     job_t J;
     memset(&J, 0, sizeof J);
     J.q = q; J.k = k; J.v = v; J.o = o; J.lse = lse; J.p = NULL;
     J.bh = b * h; J.sq = sq; J.sk = sk; J.d = d; J.scale = scale;
-    J.causal = causal ? 1 : 0; J.mut = mutant;
+    J.causal = causal ? 1 : 0;
     return run_threads(J, nthreads);
-}
-
-int oracle_attn(const double* q, const double* k, const double* v, double* o,
-                double* lse, int64_t b, int64_t h, int64_t sq, int64_t sk,
-                int64_t d, double scale, int causal, int nthreads)
-{
-    return oracle_attn_mutant(q, k, v, o, lse, b, h, sq, sk, d, scale, causal,
-                              MUT_NONE, nthreads);
 }
 
 int oracle_attn_rows(const double* q, const double* k, const double* v,
@@ -283,7 +234,7 @@ int oracle_attn_rows(const double* q, const double* k, const double* v,
     memset(&J, 0, sizeof J);
     J.q = q; J.k = k; J.v = v; J.o = o; J.lse = lse; J.p = NULL;
     J.bh = b * h; J.sq = sq; J.sk = sk; J.d = d; J.scale = scale;
-    J.causal = causal ? 1 : 0; J.mut = MUT_NONE;
+    J.causal = causal ? 1 : 0;
     J.rows = rows; J.nrows = nrows;
     return run_threads(J, nthreads);
 }
@@ -299,7 +250,7 @@ int oracle_attn_probs(const double* q, const double* k, const double* v,
     memset(&J, 0, sizeof J);
     J.q = q; J.k = k; J.v = v; J.o = o; J.lse = lse; J.p = p;
     J.bh = b * h; J.sq = sq; J.sk = sk; J.d = d; J.scale = scale;
-    J.causal = causal ? 1 : 0; J.mut = MUT_NONE;
+    J.causal = causal ? 1 : 0;
     return run_threads(J, 1);
 }
 
@@ -447,20 +398,12 @@ int oracle_attn_online_q_outer(const double* q, const double* k,
 /* Heads run in parallel; each thread owns whole heads.                      */
 /* ------------------------------------------------------------------------ */
 
-enum {
-    BMUT_NONE = 0,
-    BMUT_NO_D = 1,          /* dS = P dP (the row term D forgotten)          */
-    BMUT_DK_NO_SCALE = 2,   /* dK misses the scale                           */
-    BMUT_DV_USES_DP = 3,    /* dV accumulates dP-weighted dO instead of P    */
-    BMUT_DQ_USES_V = 4      /* dQ sums dS_ij v_j instead of dS_ij k_j        */
-};
-
 typedef struct {
     const double *q, *k, *v, *dout;
     double *dq, *dk, *dv;
     int64_t bh, sq, sk, d;
     double scale;
-    int causal, mut, tid, nthreads, status;
+    int causal, tid, nthreads, status;
 } bjob_t;
 
 static void* run_bwd(void* arg)
@@ -488,8 +431,8 @@ static void* run_bwd(void* arg)
         for (int64_t i = 0; i < sq; ++i) {
             const double* qi = qh + i * d;
             const double* gi = gh + i * d;
-            (void)attend_row(qi, kh, vh, i, sk, d, J->scale, J->causal, MUT_NONE, s, oi, p);
-            const int64_t n = key_limit(i, sk, J->causal, MUT_NONE);
+            (void)attend_row(qi, kh, vh, i, sk, d, J->scale, J->causal, s, oi, p);
+            const int64_t n = key_limit(i, sk, J->causal);
             double Di = 0.0;
             for (int64_t j = 0; j < n; ++j) {
                 dp[j] = dot(gi, vh + j * d, d);
@@ -498,18 +441,14 @@ static void* run_bwd(void* arg)
             double* dqi = dqh + i * d;
             for (int64_t x = 0; x < d; ++x) dqi[x] = 0.0;
             for (int64_t j = 0; j < n; ++j) {
-                const double ds = p[j] * (J->mut == BMUT_NO_D ? dp[j] : dp[j] - Di);
+                const double ds = p[j] * (dp[j] - Di);
                 const double* kj = kh + j * d;
-                const double* vj = vh + j * d;
-                const double* src = (J->mut == BMUT_DQ_USES_V) ? vj : kj;
-                const double wv = (J->mut == BMUT_DV_USES_DP) ? dp[j] : p[j];
-                const double sk_ = (J->mut == BMUT_DK_NO_SCALE) ? 1.0 : J->scale;
                 double* dkj = dkh + j * d;
                 double* dvj = dvh + j * d;
                 for (int64_t x = 0; x < d; ++x) {
-                    dqi[x] += J->scale * ds * src[x];
-                    dkj[x] += sk_ * ds * qi[x];
-                    dvj[x] += wv * gi[x];
+                    dqi[x] += J->scale * ds * kj[x];
+                    dkj[x] += J->scale * ds * qi[x];
+                    dvj[x] += p[j] * gi[x];
                 }
             }
         }
@@ -521,7 +460,7 @@ static void* run_bwd(void* arg)
 int oracle_attn_bwd(const double* q, const double* k, const double* v,
                     const double* dout, double* dq, double* dk, double* dv,
                     int64_t b, int64_t h, int64_t sq, int64_t sk, int64_t d,
-                    double scale, int causal, int mutant, int nthreads)
+                    double scale, int causal, int nthreads)
 {
     if (!q || !k || !v || !dout || !dq || !dk || !dv || bad_dims(b, h, sq, sk, d))
         return -1;
@@ -534,7 +473,7 @@ int oracle_attn_bwd(const double* q, const double* k, const double* v,
         memset(&J, 0, sizeof J);
         J.q = q; J.k = k; J.v = v; J.dout = dout; J.dq = dq; J.dk = dk; J.dv = dv;
         J.bh = b * h; J.sq = sq; J.sk = sk; J.d = d; J.scale = scale;
-        J.causal = causal ? 1 : 0; J.mut = mutant; J.tid = t; J.nthreads = nthreads;
+        J.causal = causal ? 1 : 0; J.tid = t; J.nthreads = nthreads;
         jobs[t] = J;
     }
     int started = 0;
