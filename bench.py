@@ -68,6 +68,91 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+class ClockSampler:
+    """Samples the graphics (shader) clock of the GPU that runs the kernels,
+    in MHz, from amdsmi every ``period`` seconds in a background thread while
+    the timed launches run.  Reports None when amdsmi is unavailable or the
+    device cannot be matched."""
+
+    def __init__(self, torch_mod, period: float = 0.01):
+        import threading
+        self.samples = []
+        self.period = period
+        self.error = None
+        self._stop = threading.Event()
+        self._thread = None
+        self._handle = None
+        self._smi = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            handles = amdsmi.amdsmi_get_processor_handles()
+            want = None
+            try:
+                props = torch_mod.cuda.get_device_properties(torch_mod.cuda.current_device())
+                want = int(getattr(props, "pci_bus_id"))
+            except Exception:  # noqa: BLE001 - older torch: no bus id
+                want = None
+            chosen = None
+            for h in handles:
+                bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)  # "dddd:bb:dd.f"
+                if want is not None and int(bdf.split(":")[1], 16) == want:
+                    chosen = h
+            if chosen is None and len(handles) == 1:
+                chosen = handles[0]
+            if chosen is None:
+                self.error = "device not matched among %d amdsmi handles" % len(handles)
+            else:
+                self._handle, self._smi = chosen, amdsmi
+                self.read()  # fails here, not in the thread, if clocks are not readable
+        except Exception as e:  # noqa: BLE001 - report, never fail the bench
+            self.error = "amdsmi: %s" % e
+            self._handle = None
+
+    def read(self) -> float:
+        info = self._smi.amdsmi_get_clock_info(self._handle, self._smi.AmdSmiClkType.GFX)
+        return float(info["clk"])
+
+    def _run(self):
+        while not self._stop.wait(self.period):
+            try:
+                self.samples.append(self.read())
+            except Exception as e:  # noqa: BLE001
+                self.error = "amdsmi: %s" % e
+                return
+
+    def start(self):
+        if self._handle is not None:
+            import threading
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+
+    def stop(self):
+        if self._thread is not None:
+            self._stop.set()
+            self._thread.join()
+
+    def summary(self):
+        if not self.samples:
+            return {"mhz_median": None, "samples": 0, "source": "amdsmi GFX clock",
+                    "error": self.error}
+        s = sorted(self.samples)
+        return {"mhz_median": s[len(s) // 2], "mhz_min": s[0], "mhz_max": s[-1],
+                "samples": len(s), "source": "amdsmi GFX clock, sampled every %.0f ms during the "
+                "timed launches" % (self.period * 1e3)}
+
+
 def kernel_sha() -> str:
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
@@ -112,7 +197,7 @@ def cpu_baseline(w: W.Workload, q, k, v, budget_s: float):
     dt = time.perf_counter() - t0
     flops = head_flops * nheads
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": nthreads,
-            "kind": "oracle",
+            "cpu_model": cpu_model(), "kind": "oracle",
             "sample": "%d of %d heads (full sq=%d x sk=%d each), fp64 C oracle, %.1f s" % (
                 nheads, w.b * w.h, w.sq, w.sk, dt)}
 
@@ -136,7 +221,7 @@ def cpu_baseline_bwd(w: W.Workload, q, k, v, budget_s: float):
     oracle.attn_bwd(sl(q, w.sq), sl(k, w.sk), sl(v, w.sk), sl(g, w.sq), scale, w.causal, nthreads=nthreads)
     dt = time.perf_counter() - t0
     return {"value": head_flops * nheads / dt / 1e12, "unit": "TFLOP/s", "cores": min(nthreads, nheads),
-            "kind": "oracle",
+            "cpu_model": cpu_model(), "kind": "oracle",
             "sample": "backward of %d of %d heads (full sq=%d x sk=%d each), fp64 C oracle, %.1f s" % (
                 nheads, w.b * w.h, w.sq, w.sk, dt)}
 
@@ -144,7 +229,7 @@ def cpu_baseline_bwd(w: W.Workload, q, k, v, budget_s: float):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=W.HEADLINE.name, choices=sorted(W.BY_NAME))
     ap.add_argument("--split", type=int, default=1, metavar="N",
@@ -253,9 +338,12 @@ def main():
             torch.cuda.synchronize()
     torch.cuda.synchronize()
 
-    # per-launch kernel time: HIP events on the launch stream around each call
+    # per-launch kernel time: HIP events on the launch stream around each call;
+    # the shader clock is sampled alongside
+    clock = ClockSampler(torch)
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
+    clock.start()
     t0 = time.perf_counter()
     evs[0].record(stream)
     for i in range(args.steps):
@@ -263,8 +351,10 @@ def main():
         evs[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    clock.stop()
     per = [evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)]
     avg_ms = sum(per) / len(per)
+    med_ms = sorted(per)[len(per) // 2]
     ms_per_step = wall * 1e3 / args.steps
 
     flops = w.flops * (2.5 if args.bwd else 1.0)
@@ -272,11 +362,17 @@ def main():
     achieved = flops / (avg_ms * 1e-3) / 1e12
     dtype = "fp8_e4m3" if args.fp8 else w.dtype
     peak = PEAK_TFLOPS[dtype]
+    log("[bench] shader clock: %s" % clock.summary())
     log("[bench] %s: wall %.3f ms/step, kernel avg %.3f ms (min %.3f, max %.3f), "
         "%.1f TFLOP/s = %.1f%% of %.1f; %.0f GB/s algorithmic" % (
             w.name, ms_per_step, avg_ms, min(per), max(per), achieved,
             100 * achieved / peak, peak, w.algorithmic_bytes / (avg_ms * 1e-3) / 1e9))
 
+    sclk = clock.summary()
+    # the matrix peak scales with the shader clock: % of peak at the clock seen
+    frac_sclk = None
+    if sclk.get("mhz_median"):
+        frac_sclk = round(achieved / (peak * sclk["mhz_median"] / 2400.0), 4)
     kernel = "fa_bwd" if args.bwd else ("fa_fwd_fp8" if args.fp8 else
                                          ("fa_fwd" if args.split == 1 else "fa_fwd_split"))
     out = {
@@ -296,6 +392,15 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": traffic_record(w) if kernel == "fa_fwd" else None},
+        "kernel_us": {"mean": round(avg_ms * 1e3, 2), "median": round(med_ms * 1e3, 2),
+                      "min": round(min(per) * 1e3, 2), "max": round(max(per) * 1e3, 2),
+                      "calls": args.steps, "timed_ms": round(sum(per), 1)},
+        "tflops_at_median": round(flops / (med_ms * 1e-3) / 1e12, 3),
+        "gbps_algorithmic": round(w.algorithmic_bytes / (avg_ms * 1e-3) / 1e9, 1),
+        "hbm_frac_algorithmic": round(w.algorithmic_bytes / (avg_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "sclk": sclk,
+        "peak_at_sclk": None if frac_sclk is None else round(peak * sclk["mhz_median"] / 2400.0, 1),
+        "frac_at_sclk": frac_sclk,
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on a sample (~%.0f s)" % args.cpu_budget)

@@ -163,6 +163,24 @@ def _dtype_code(t) -> int:
     return codes[t.dtype]
 
 
+def _check_buffer(name, t, shape, dtype, device):
+    """A caller-supplied output or workspace must be a contiguous tensor of
+    the given shape and dtype on the given device: the kernels write exactly
+    the elements the input sizes imply, so a smaller or wrongly typed buffer
+    would be written past its end or filled with the wrong encoding."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise FaError(FA_ERR_INVALID_ARG, "%s must be a torch tensor" % name)
+    if t.device != device:
+        raise FaError(FA_ERR_INVALID_ARG, "%s must be on %s (got %s)" % (name, device, t.device))
+    if dtype is not None and t.dtype != dtype:
+        raise FaError(FA_ERR_INVALID_ARG, "%s must be %s (got %s)" % (name, dtype, t.dtype))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise FaError(FA_ERR_INVALID_ARG, "%s must have shape %s (got %s)" % (name, tuple(shape), tuple(t.shape)))
+    if not t.is_contiguous():
+        raise FaError(FA_ERR_INVALID_ARG, "%s must be contiguous" % name)
+
+
 def attention(q, k, v, causal: bool = False, scale: float | None = None, out=None,
               lse=None, stream=None, nsplit: int = 1, workspace=None):
     """O, LSE for torch device tensors q [b,h,sq,d], k/v [b,h,sk,d].
@@ -183,6 +201,12 @@ def attention(q, k, v, causal: bool = False, scale: float | None = None, out=Non
         raise FaError(FA_ERR_INVALID_ARG, "q, k, v must be contiguous")
     if not (q.dtype == k.dtype == v.dtype):
         raise FaError(FA_ERR_INVALID_ARG, "q, k, v must share a dtype")
+    if out is not None:
+        _check_buffer("out", out, (b, h, sq, d), q.dtype, q.device)
+    if lse is not None:
+        _check_buffer("lse", lse, (b, h, sq), torch.float32, q.device)
+    if workspace is not None:
+        _check_buffer("workspace", workspace, None, None, q.device)
     if not (q.is_cuda and k.is_cuda and v.is_cuda):
         raise FaError(FA_ERR_INVALID_ARG, "q, k, v must be device tensors")
     if scale is None:
@@ -220,6 +244,12 @@ def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_sq: int, causal: b
     total_k = k.shape[1]
     if tuple(k.shape) != (h, total_k, d) or tuple(v.shape) != (h, total_k, d):
         raise FaError(FA_ERR_INVALID_ARG, "k and v must be [h, total_k, d] matching q")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise FaError(FA_ERR_INVALID_ARG, "q, k, v must share a dtype")
+    if out is not None:
+        _check_buffer("out", out, (h, total_q, d), q.dtype, q.device)
+    if lse is not None:
+        _check_buffer("lse", lse, (h, total_q), torch.float32, q.device)
     for t in (q, k, v, cu_seqlens_q, cu_seqlens_k):
         if not (t.is_cuda and t.is_contiguous()):
             raise FaError(FA_ERR_INVALID_ARG, "all tensors must be contiguous device tensors")
@@ -260,11 +290,16 @@ def attention_bwd(q, k, v, out, lse, dout, causal: bool = False, scale: float | 
         raise FaError(FA_ERR_INVALID_ARG, "out and dout must have q's shape")
     if tuple(lse.shape) != (b, h, sq) or lse.dtype != torch.float32:
         raise FaError(FA_ERR_INVALID_ARG, "lse must be fp32 [b, h, sq]")
+    if not (q.dtype == k.dtype == v.dtype == out.dtype == dout.dtype):
+        raise FaError(FA_ERR_INVALID_ARG, "q, k, v, out, dout must share a dtype")
+    for name, t, shp in (("dq", dq, (b, h, sq, d)), ("dk", dk, (b, h, sk, d)), ("dv", dv, (b, h, sk, d))):
+        if t is not None:
+            _check_buffer(name, t, shp, q.dtype, q.device)
+    if workspace is not None:
+        _check_buffer("workspace", workspace, None, None, q.device)
     for t in (q, k, v, out, lse, dout):
         if not (t.is_cuda and t.is_contiguous()):
             raise FaError(FA_ERR_INVALID_ARG, "all tensors must be contiguous device tensors")
-    if not (q.dtype == k.dtype == v.dtype == out.dtype == dout.dtype):
-        raise FaError(FA_ERR_INVALID_ARG, "q, k, v, out, dout must share a dtype")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     dq = torch.empty_like(q) if dq is None else dq
@@ -296,10 +331,15 @@ def attention_fp8(q, k, v, causal: bool = False, scale: float | None = None, des
     if tuple(k.shape) != (b, h, sk, d) or tuple(v.shape) != (b, h, sk, d):
         raise FaError(FA_ERR_INVALID_ARG, "k and v must be [b, h, sk, d] matching q")
     for t in (q, k, v):
-        if not (t.is_cuda and t.is_contiguous()):
-            raise FaError(FA_ERR_INVALID_ARG, "q, k, v must be contiguous device tensors")
         if t.dtype not in (torch.float8_e4m3fn, torch.uint8):
             raise FaError(FA_ERR_UNSUPPORTED, "q, k, v must be float8_e4m3fn (or its uint8 bytes)")
+    if out is not None:
+        _check_buffer("out", out, (b, h, sq, d), torch.bfloat16, q.device)
+    if lse is not None:
+        _check_buffer("lse", lse, (b, h, sq), torch.float32, q.device)
+    for t in (q, k, v):
+        if not (t.is_cuda and t.is_contiguous()):
+            raise FaError(FA_ERR_INVALID_ARG, "q, k, v must be contiguous device tensors")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:

@@ -322,3 +322,70 @@ def test_fp8_binding_rejects_wrong_dtype():
     with pytest.raises(fa.FaError):
         fa.attention_fp8(x, x, x)
 
+
+
+# ---- caller-supplied outputs and workspaces (checked by the binding, which
+#      is the only place that knows the tensors' sizes and types) ----
+def _bad_outputs():
+    import torch
+    bf = torch.bfloat16
+    return [
+        ("out", dict(out=torch.empty(1, 2, 7, 64, dtype=bf)), "shape"),           # too small
+        ("out", dict(out=torch.empty(1, 2, 8, 64, dtype=torch.float16)), "must be"),  # wrong dtype
+        ("out", dict(out=torch.empty(1, 2, 64, 8, dtype=bf).transpose(2, 3)), "contiguous"),
+        ("out", dict(out=[0]), "torch tensor"),
+        ("lse", dict(lse=torch.empty(1, 2, 7)), "shape"),
+        ("lse", dict(lse=torch.empty(1, 2, 8, dtype=torch.float64)), "must be"),
+        ("lse", dict(lse=torch.empty(1, 2, 8, dtype=bf)), "must be"),
+        ("workspace", dict(workspace=torch.empty(64, dtype=torch.uint8, device="meta")), "must be on"),
+    ]
+
+
+@pytest.mark.parametrize("name,kw,what", _bad_outputs(), ids=lambda x: x if isinstance(x, str) else "")
+def test_attention_rejects_bad_caller_buffers(name, kw, what):
+    import torch
+    q = torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(fa.FaError) as e:
+        fa.attention(q, q, q, **kw)
+    assert e.value.code == fa.FA_ERR_INVALID_ARG
+    assert name in str(e.value) and what in str(e.value)
+
+
+def test_attention_varlen_rejects_bad_caller_buffers():
+    import torch
+    q = torch.zeros(2, 10, 64, dtype=torch.bfloat16)
+    cu = torch.tensor([0, 10], dtype=torch.int32)
+    for kw, name in [(dict(out=torch.empty(2, 9, 64, dtype=torch.bfloat16)), "out"),
+                     (dict(out=torch.empty(2, 10, 64, dtype=torch.float32)), "out"),
+                     (dict(lse=torch.empty(2, 10, dtype=torch.float16)), "lse"),
+                     (dict(lse=torch.empty(10, 2)), "lse")]:
+        with pytest.raises(fa.FaError) as e:
+            fa.attention_varlen(q, q, q, cu, cu, 10, **kw)
+        assert e.value.code == fa.FA_ERR_INVALID_ARG and name in str(e.value)
+
+
+def test_attention_bwd_rejects_bad_caller_buffers():
+    import torch
+    bf = torch.bfloat16
+    q = torch.zeros(1, 2, 8, 128, dtype=bf)
+    k = torch.zeros(1, 2, 5, 128, dtype=bf)
+    lse = torch.zeros(1, 2, 8)
+    for kw, name in [(dict(dq=torch.empty(1, 2, 5, 128, dtype=bf)), "dq"),     # k's shape, not q's
+                     (dict(dk=torch.empty(1, 2, 8, 128, dtype=bf)), "dk"),     # q's shape, not k's
+                     (dict(dv=torch.empty(1, 2, 5, 128, dtype=torch.float16)), "dv"),
+                     (dict(dq=torch.empty(1, 2, 128, 8, dtype=bf).transpose(2, 3)), "dq"),
+                     (dict(workspace=torch.empty(64, dtype=torch.uint8, device="meta")), "workspace")]:
+        with pytest.raises(fa.FaError) as e:
+            fa.attention_bwd(q, k, k, q, lse, q, **kw)
+        assert e.value.code == fa.FA_ERR_INVALID_ARG and name in str(e.value)
+
+
+def test_attention_fp8_rejects_bad_caller_buffers():
+    import torch
+    x = torch.zeros(1, 1, 4, 128, dtype=torch.uint8)
+    for kw, name in [(dict(out=torch.empty(1, 1, 4, 128, dtype=torch.float16)), "out"),  # O is bf16
+                     (dict(out=torch.empty(1, 1, 3, 128, dtype=torch.bfloat16)), "out"),
+                     (dict(lse=torch.empty(1, 1, 4, dtype=torch.bfloat16)), "lse")]:
+        with pytest.raises(fa.FaError) as e:
+            fa.attention_fp8(x, x, x, **kw)
+        assert e.value.code == fa.FA_ERR_INVALID_ARG and name in str(e.value)

@@ -5,15 +5,16 @@ Tolerances (max-abs over every compared element): O within 1e-5 (fp32),
 inputs (``workloads``), the oracle widening the stored fp32/fp16/bf16 values
 exactly to fp64, and both use the fp32 value of the scale.
 
-* small and medium shapes (the oracle finishes in seconds) are compared
-  element by element over the whole output, and span several tiles in both
-  sequence dimensions with ragged tails;
-* the five benchmark workloads run at full size in the launch configuration
-  the benchmark times, compared on sampled rows -- every row of the first and
-  last query tiles of a few heads, rows at tile boundaries and the causal
-  diagonal, and random rows -- which the oracle computes one by one;
-* invariants that hold at any size (constant V, one-hot selection, causal
-  row 0, convex-combination bound, bitwise determinism).
+* the five benchmark workloads run at full size, in the launch configuration
+  the benchmark times, and are compared element by element over the whole
+  output (every O element and every LSE row of every head);
+* small and medium shapes span several tiles in both sequence dimensions
+  with ragged tails, compared the same way;
+* sampled rows of the large workloads (first and last query tiles, tile
+  boundaries, the causal diagonal) as an extra, and invariants that hold at
+  any size (constant V, one-hot selection, causal row 0, convex-combination
+  bound, bitwise determinism of the 4-wave and the 8-wave kernel, and the
+  8-wave kernel bit-for-bit equal to the 4-wave kernel on the same rows).
 """
 import math
 import sys
@@ -87,9 +88,14 @@ def sample_rows(w: W.Workload, block_m: int, seed=0, heads=4, random_rows=48):
     return np.array(sorted(rows), dtype=np.int64)
 
 
-@pytest.mark.parametrize("idx", [0, 1])
+@pytest.mark.parametrize("idx", range(len(W.WORKLOADS)), ids=[w.name for w in W.WORKLOADS])
 def test_workload_full_compare(idx, gpu):
-    compare_full(W.WORKLOADS[idx])
+    """Every element of O and LSE of each benchmark workload at full size."""
+    w = W.WORKLOADS[idx]
+    cfg = fa.fa_query_config(W.DTYPE_CODE[w.dtype], w.d, int(w.causal), w.b, w.h, w.sq, w.sk)
+    note(f"  kernel tiling {cfg}")
+    eo, el = compare_full(w)
+    note(f"  O max-abs={eo:.3e} LSE max-abs={el:.3e}")
 
 
 @pytest.mark.slow
@@ -153,6 +159,8 @@ PINGPONG = [
     ("bf16", 1, 256, 300, 300, 128, True),
     ("f16", 2, 128, 260, 260, 128, False),
     ("bf16", 1, 256, 200, 333, 128, True),
+    ("bf16", 1, 256, 333, 200, 128, True),   # causal sq > sk: rows past sk see every key
+    ("f16", 1, 512, 520, 130, 128, True),
 ]
 
 
@@ -222,14 +230,42 @@ def test_one_hot_wide_score_range(dt, d, sk, gpu):
     assert float(np.abs(lse[0, 0].double().cpu().numpy() - (64.0 + np.log(cnt))).max()) <= TOL_LSE
 
 
-def test_deterministic(gpu):
+@pytest.mark.parametrize("b,h,sq,waves", [(2, 4, 777, 4), (1, 256, 4096, 8)])
+def test_deterministic(b, h, sq, waves, gpu):
+    """Two runs give the same bits, for the 4-wave kernel and for the 8-wave
+    ping-pong kernel (which has no barrier between the two slots of a key
+    window, so a race on an LDS stage would show up as run-to-run noise)."""
     import torch
-    w = W.shape("det", "bf16", 2, 4, 777, 777, 128, True, seed=9)
+    cfg = fa.fa_query_config(W.DTYPE_CODE["bf16"], 128, 1, b, h, sq, sq)
+    assert cfg["waves"] == waves
+    w = W.shape("det", "bf16", b, h, sq, sq, 128, True, seed=9)
     q, k, v = (t.cuda() for t in W.make(w))
     o1, l1 = fa.attention(q, k, v, causal=True)
     o2, l2 = fa.attention(q, k, v, causal=True)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("dt,h,sq,sk,causal", [("bf16", 256, 4096, 4096, True), ("f16", 256, 333, 200, True),
+                                              ("bf16", 300, 260, 390, False)])
+def test_eight_waves_equal_four_waves(dt, h, sq, sk, causal, gpu):
+    """The same problem through the 8-wave ping-pong kernel (fa_fwd on many
+    heads) and through the 4-wave kernel (fa_fwd_varlen with one sequence per
+    head set) gives the same bits: both run each 32-row query block through
+    the same instruction sequence per 64-key tile, so any difference means a
+    stage was read before its copy landed or after it was overwritten."""
+    import torch
+    cfg = fa.fa_query_config(W.DTYPE_CODE[dt], 128, int(causal), 1, h, sq, sk)
+    assert cfg["waves"] == 8
+    w = W.shape("waves", dt, 1, h, sq, sk, 128, causal, seed=sq + sk)
+    q, k, v = (t.cuda() for t in W.make(w))
+    s = scale32(w.scale)
+    o8, l8 = fa.attention(q, k, v, causal=causal, scale=s)
+    cu_q = torch.tensor([0, sq], dtype=torch.int32, device="cuda")
+    cu_k = torch.tensor([0, sk], dtype=torch.int32, device="cuda")
+    o4, l4 = fa.attention_varlen(q[0], k[0], v[0], cu_q, cu_k, sq, causal=causal, scale=s)
+    torch.cuda.synchronize()
+    assert torch.equal(o8[0], o4) and torch.equal(l8[0], l4)
 
 
 def test_stream_argument(gpu):
