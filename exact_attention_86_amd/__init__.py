@@ -12,6 +12,9 @@ raise.
                  workspace, workspace_bytes, stream)
         split-KV forward; fa_split_workspace_bytes(b, h, sq, d, nsplit) sizes
         its workspace
+    fa_fwd_split_noalloc(q, k, v, o, lse, b, h, sq, sk, d, scale, causal, dtype,
+                         nsplit, stream)
+        the same with the library's own per-GPU scratch (allocates nothing)
     fa_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, batch, h, total_q,
                   total_k, max_sq, d, scale, causal, dtype, stream)
         packed variable-length sequences
@@ -72,6 +75,9 @@ def lib() -> ctypes.CDLL:
                                    ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                    vp, ctypes.c_size_t, vp]
         L.fa_fwd_split.restype = ctypes.c_int
+        L.fa_fwd_split_noalloc.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                                           ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
+        L.fa_fwd_split_noalloc.restype = ctypes.c_int
         L.fa_split_workspace_bytes.argtypes = [i64, i64, i64, i64, ctypes.c_int]
         L.fa_split_workspace_bytes.restype = ctypes.c_size_t
         L.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
@@ -120,6 +126,18 @@ def fa_fwd_split(q, k, v, o, lse, b, h, sq, sk, d, scale, causal, dtype, nsplit,
     return lib().fa_fwd_split(q, k, v, o, lse, int(b), int(h), int(sq), int(sk), int(d),
                               float(scale), int(causal), int(dtype), int(nsplit), workspace,
                               int(workspace_bytes), stream)
+
+
+def fa_fwd_split_noalloc(q, k, v, o, lse, b, h, sq, sk, d, scale, causal, dtype, nsplit,
+                         stream) -> int:
+    """The split-KV C entry point that allocates nothing (library-owned
+    scratch of FA_NOALLOC_SCRATCH_BYTES per GPU): device addresses as ints,
+    returns the status code."""
+    return lib().fa_fwd_split_noalloc(q, k, v, o, lse, int(b), int(h), int(sq), int(sk), int(d),
+                                      float(scale), int(causal), int(dtype), int(nsplit), stream)
+
+
+FA_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 def fa_split_workspace_bytes(b, h, sq, d, nsplit) -> int:

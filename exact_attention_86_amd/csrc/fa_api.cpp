@@ -108,9 +108,14 @@ static int check_common(const char* who, const void* q, const void* k, const voi
     return FA_OK;
 }
 
+// nsplit * b * h * sq * (d + 1) * 4, saturated at SIZE_MAX (callers have
+// bounded every factor to 31 bits, but their product can exceed 64 bits)
 static size_t split_ws_bytes(int64_t b, int64_t h, int64_t sq, int64_t d, int64_t nsplit)
 {
-    return (size_t)nsplit * (size_t)(b * h * sq) * (size_t)(d + 1) * 4;
+    unsigned __int128 n = (unsigned __int128)nsplit * (unsigned __int128)(b * h);
+    n *= (unsigned __int128)sq;
+    n *= (unsigned __int128)(d + 1) * 4u;
+    return n > (unsigned __int128)SIZE_MAX ? SIZE_MAX : (size_t)n;
 }
 
 FA_API int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -150,37 +155,61 @@ FA_API size_t fa_split_workspace_bytes(int64_t b, int64_t h, int64_t sq, int64_t
     return split_ws_bytes(b, h, sq, d, nsplit);
 }
 
-FA_API int fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse,
-                        int64_t b, int64_t h, int64_t sq, int64_t sk, int64_t d, float scale,
-                        int causal, int dtype, int nsplit, void* workspace, size_t workspace_bytes,
-                        void* stream)
+// the split-KV forward with its partial results in `workspace` (the caller's
+// buffer, or the library's scratch when `noalloc`); `who` prefixes messages
+static int fwd_split(const char* who, const void* q, const void* k, const void* v, void* o, float* lse,
+                     int64_t b, int64_t h, int64_t sq, int64_t sk, int64_t d, float scale, int causal,
+                     int dtype, int nsplit, void* workspace, size_t workspace_bytes, bool noalloc,
+                     void* stream)
 {
-    if (nsplit < 1 || nsplit > FA_MAX_SPLIT)
-        return fail(FA_ERR_INVALID_ARG, "fa_fwd_split: nsplit must be in [1, 64]");
-    if (nsplit == 1)  // one part: exactly fa_fwd; the workspace is not touched
+    char msg[192];
+    auto bad = [&](int code, const char* what) {
+        snprintf(msg, sizeof msg, "%s: %s", who, what);
+        return fail(code, msg);
+    };
+    if (nsplit < 1 || nsplit > FA_MAX_SPLIT) return bad(FA_ERR_INVALID_ARG, "nsplit must be in [1, 64]");
+    if (nsplit == 1)  // one part: exactly fa_fwd; no workspace is touched
         return fa_fwd(q, k, v, o, lse, b, h, sq, sk, d, scale, causal, dtype, stream);
     fa::Params p;
-    const int rc = check_common("fa_fwd_split", q, k, v, o, lse, b, h, sq, sk, d, scale, causal, dtype, &p);
+    const int rc = check_common(who, q, k, v, o, lse, b, h, sq, sk, d, scale, causal, dtype, &p);
     if (rc != FA_OK) return rc;
     fa::TileConfig tc;
     if (!fa::tile_config_split(dtype, (int)d, &tc))
-        return fail(FA_ERR_UNSUPPORTED, "fa_fwd_split: fp16/bf16 with d = 64, 128 or 256 only");
-    if (!workspace) return fail(FA_ERR_INVALID_ARG, "fa_fwd_split: NULL workspace");
-    if ((uintptr_t)workspace & 15u) return fail(FA_ERR_MISALIGNED, "fa_fwd_split: workspace must be 16-byte aligned");
+        return bad(FA_ERR_UNSUPPORTED, "fp16/bf16 with d = 64, 128 or 256 only");
     const size_t need = split_ws_bytes(b, h, sq, d, nsplit);
-    if (workspace_bytes < need)
-        return fail(FA_ERR_INVALID_ARG, "fa_fwd_split: workspace smaller than fa_split_workspace_bytes()");
-    const size_t nq = (size_t)(b * h * sq * d) * 2, nk = (size_t)(b * h * sk * d) * 2;
-    const size_t nl = (size_t)(b * h * sq) * 4;
-    if (overlap(workspace, need, q, nq) || overlap(workspace, need, k, nk) || overlap(workspace, need, v, nk) ||
-        overlap(workspace, need, o, nq) || overlap(workspace, need, lse, nl))
-        return fail(FA_ERR_INVALID_ARG, "fa_fwd_split: workspace must not overlap the inputs or outputs");
+    if (noalloc) {
+        if (need > FA_NOALLOC_SCRATCH_BYTES) {
+            snprintf(msg, sizeof msg, "%s: nsplit*b*h*sq*(d+1)*4 = %zu bytes exceeds the %zu-byte library scratch",
+                     who, need, (size_t)FA_NOALLOC_SCRATCH_BYTES);
+            return fail(FA_ERR_TOO_LARGE, msg);
+        }
+    } else {
+        if (!workspace) return bad(FA_ERR_INVALID_ARG, "NULL workspace");
+        if ((uintptr_t)workspace & 15u) return bad(FA_ERR_MISALIGNED, "workspace must be 16-byte aligned");
+        if (workspace_bytes < need)
+            return bad(FA_ERR_INVALID_ARG, "workspace smaller than fa_split_workspace_bytes()");
+        const size_t nq = (size_t)(b * h * sq * d) * 2, nk = (size_t)(b * h * sk * d) * 2;
+        const size_t nl = (size_t)(b * h * sq) * 4;
+        if (overlap(workspace, need, q, nq) || overlap(workspace, need, k, nk) ||
+            overlap(workspace, need, v, nk) || overlap(workspace, need, o, nq) ||
+            overlap(workspace, need, lse, nl))
+            return bad(FA_ERR_INVALID_ARG, "workspace must not overlap the inputs or outputs");
+    }
     const int64_t n_mtiles = (sq + tc.block_m - 1) / tc.block_m;
     const int64_t items_per_head = n_mtiles * nsplit;
     const int64_t n_items = b * h * items_per_head;
     const int64_t merge_blocks = (b * h * sq * (d / 8) + 255) / 256;
     if (n_items > INT32_MAX - 8 || items_per_head > INT32_MAX || merge_blocks > INT32_MAX)
-        return fail(FA_ERR_TOO_LARGE, "fa_fwd_split: too many tiles for one launch");
+        return bad(FA_ERR_TOO_LARGE, "too many tiles for one launch");
+    hipError_t e = hipSuccess;
+    if (noalloc) {
+        // every argument is valid: only now touch the runtime
+        e = fa::noalloc_scratch(&workspace);
+        if (e != hipSuccess) {
+            snprintf(msg, sizeof msg, "%s: library scratch unavailable: %s", who, hipGetErrorString(e));
+            return fail(FA_ERR_HIP, msg);
+        }
+    }
     p.n_mtiles = (int)n_mtiles;
     p.items_per_head = (int)items_per_head;
     p.n_items = (int)n_items;
@@ -188,13 +217,30 @@ FA_API int fa_fwd_split(const void* q, const void* k, const void* v, void* o, fl
     p.nsplit = nsplit;
     p.ws = (float*)workspace;
 
-    hipError_t e = fa::launch_fwd_split(dtype, (int)d, tc, p, (hipStream_t)stream);
+    e = fa::launch_fwd_split(dtype, (int)d, tc, p, (hipStream_t)stream);
     if (e != hipSuccess) {
-        snprintf(g_err, sizeof g_err, "fa_fwd_split: launch failed: %s", hipGetErrorString(e));
-        return FA_ERR_HIP;
+        snprintf(msg, sizeof msg, "%s: launch failed: %s", who, hipGetErrorString(e));
+        return fail(FA_ERR_HIP, msg);
     }
     g_err[0] = 0;
     return FA_OK;
+}
+
+FA_API int fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int64_t b, int64_t h, int64_t sq, int64_t sk, int64_t d, float scale,
+                        int causal, int dtype, int nsplit, void* workspace, size_t workspace_bytes,
+                        void* stream)
+{
+    return fwd_split("fa_fwd_split", q, k, v, o, lse, b, h, sq, sk, d, scale, causal, dtype, nsplit,
+                     workspace, workspace_bytes, false, stream);
+}
+
+FA_API int fa_fwd_split_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                                int64_t b, int64_t h, int64_t sq, int64_t sk, int64_t d, float scale,
+                                int causal, int dtype, int nsplit, void* stream)
+{
+    return fwd_split("fa_fwd_split_noalloc", q, k, v, o, lse, b, h, sq, sk, d, scale, causal, dtype,
+                     nsplit, nullptr, 0, true, stream);
 }
 
 FA_API int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,

@@ -35,6 +35,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "fa_device.h"
 #include "fa_kernels.h"
 
@@ -1085,6 +1087,36 @@ fa_combine(Params p)
     for (int e = 0; e < 4; ++e) out[e] = pack2(acc[2 * e] * inv, acc[2 * e + 1] * inv, BF16);
     *(u32x4_t*)((uint16_t*)p.o + row * D + c8) = out;
     if (c8 == 0) p.lse[row] = sum > 0.f ? m + logf(sum) : -INFINITY;
+}
+
+// ---------------------------------------------------------------------------
+// library-owned scratch for fa_fwd_split_noalloc (callers that cannot
+// allocate).  One copy of the array per GPU, held from the library's load
+// until the process ends.  In host code `scratch` names a host-side stand-in,
+// not device memory: host code only ever passes the device address that
+// hipGetSymbolAddress returns for the current device.
+// ---------------------------------------------------------------------------
+static __device__ __attribute__((aligned(256))) float scratch[kNoallocScratchBytes / sizeof(float)];
+
+hipError_t noalloc_scratch(void** ptr)
+{
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* dev_ptr[kMaxDevices] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!dev_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));  // this device's copy
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        dev_ptr[dev] = p;
+    }
+    *ptr = dev_ptr[dev];
+    return hipSuccess;
 }
 
 // ---------------------------------------------------------------------------

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fa.h"
+
 namespace fa {
 
 // Launch parameters, passed by value as the kernel argument.
@@ -81,5 +83,10 @@ hipError_t launch_fwd_fp8(const Fp8Params& p, hipStream_t stream);
 bool bwd_supported(int dtype, int d);
 hipError_t launch_bwd(int dtype, int d, const BwdParams& p, hipStream_t stream);
 hipError_t launch_fwd_split(int dtype, int d, const TileConfig& tc, const Params& p, hipStream_t stream);
+
+// Library-owned device scratch of kNoallocScratchBytes for callers that cannot
+// allocate: the current device's address of it (looked up once per device).
+constexpr size_t kNoallocScratchBytes = FA_NOALLOC_SCRATCH_BYTES;
+hipError_t noalloc_scratch(void** ptr);
 
 }  // namespace fa

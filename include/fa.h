@@ -15,7 +15,9 @@
  * names the causal variant and the forward entry point this library mirrors.
  *
  * Everything is asynchronous on the caller's HIP stream; the library keeps no
- * state between calls and allocates no device memory.
+ * state between calls and allocates no device memory (the one exception is
+ * the fixed per-GPU scratch array behind fa_fwd_split_noalloc, which exists
+ * from the library's load on).
  */
 #ifndef FA_H
 #define FA_H
@@ -132,6 +134,34 @@ FA_API int fa_fwd_split(const void* q, const void* k, const void* v, void* o,
                         float* lse, int64_t b, int64_t h, int64_t sq, int64_t sk,
                         int64_t d, float scale, int causal, int dtype, int nsplit,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fa_fwd_split_noalloc -- fa_fwd_split for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the partial results go to a scratch array the
+ * library owns instead of a caller workspace.  Same arguments as
+ * fa_fwd_split without workspace and workspace_bytes; same results, bit for
+ * bit (the same kernels run).
+ *
+ * The scratch is a FA_NOALLOC_SCRATCH_BYTES device array, one copy per GPU,
+ * held from the library's load until the process ends; its device address is
+ * looked up once per device, on the first call with that device current.  The
+ * call allocates nothing (no hipMalloc, hipFree or allocating library
+ * routine) and needs no clearing of the scratch: every partial result is
+ * written before it is read.  Every call on one GPU shares that GPU's scratch,
+ * so calls that overlap in time on one GPU (different streams, or different
+ * threads without ordering) race and give wrong results: order them.
+ *
+ * Returns FA_ERR_TOO_LARGE when nsplit * b * h * sq * (d + 1) * 4 exceeds
+ * FA_NOALLOC_SCRATCH_BYTES (checked before any HIP call), FA_ERR_HIP when the
+ * scratch address cannot be obtained, otherwise as fa_fwd_split.  nsplit = 1
+ * is exactly fa_fwd.
+ */
+#define FA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+FA_API int fa_fwd_split_noalloc(const void* q, const void* k, const void* v, void* o,
+                                float* lse, int64_t b, int64_t h, int64_t sq, int64_t sk,
+                                int64_t d, float scale, int causal, int dtype, int nsplit,
+                                void* stream);
 
 /* fa_split_workspace_bytes -- workspace size fa_fwd_split needs:
  * nsplit * b * h * sq * (d + 1) * 4 bytes (partial O and LSE in fp32); 0 for

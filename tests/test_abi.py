@@ -28,7 +28,8 @@ def declared_symbols():
 
 
 def test_header_declares_the_entry_points():
-    assert set(declared_symbols()) == {"fa_fwd", "fa_fwd_split", "fa_split_workspace_bytes",
+    assert set(declared_symbols()) == {"fa_fwd", "fa_fwd_split", "fa_fwd_split_noalloc",
+                                       "fa_split_workspace_bytes",
                                        "fa_fwd_varlen", "fa_query_config", "fa_last_error",
                                        "fa_version", "fa_bwd", "fa_bwd_workspace_bytes",
                                        "fa_fwd_fp8"}
@@ -389,3 +390,27 @@ def test_attention_fp8_rejects_bad_caller_buffers():
         with pytest.raises(fa.FaError) as e:
             fa.attention_fp8(x, x, x, **kw)
         assert e.value.code == fa.FA_ERR_INVALID_ARG and name in str(e.value)
+
+
+# ---- fa_fwd_split_noalloc: size limit checked before any HIP call ----
+def test_noalloc_scratch_limit_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define FA_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == fa.FA_NOALLOC_SCRATCH_BYTES
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(nsplit=64, sq=1 << 12), fa.FA_ERR_TOO_LARGE),   # 64 * 2 * 4096 * 129 * 4 > 64 MiB
+    (dict(nsplit=2, b=4, h=32, sq=1 << 12), fa.FA_ERR_TOO_LARGE),
+    (dict(nsplit=0), fa.FA_ERR_INVALID_ARG),
+    (dict(nsplit=65), fa.FA_ERR_INVALID_ARG),
+    (dict(nsplit=4, q=0), fa.FA_ERR_INVALID_ARG),
+    (dict(nsplit=4, dtype=fa.FA_F32), fa.FA_ERR_UNSUPPORTED),
+    (dict(nsplit=4, d=96), fa.FA_ERR_UNSUPPORTED),
+])
+def test_noalloc_invalid_arguments_rejected_before_launch(kw, code):
+    args = dict(q=Q, k=K, v=V, o=O, lse=L, b=1, h=2, sq=40, sk=50, d=128, scale=0.125, causal=0,
+                dtype=fa.FA_BF16, nsplit=4, stream=None)
+    args.update(kw)
+    assert fa.fa_fwd_split_noalloc(**args) == code
+    assert fa.fa_last_error().startswith("fa_fwd")
