@@ -232,6 +232,9 @@ def main():
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=W.HEADLINE.name, choices=sorted(W.BY_NAME))
+    ap.add_argument("--shape", default=None, metavar="DT,B,H,SQ,SK,D,CAUSAL",
+                    help="time an ad-hoc shape instead of a named workload, e.g. bf16,1,36,16384,16384,128,1 "
+                         "(N(0,1) inputs, seed 0, scale 1/sqrt(d))")
     ap.add_argument("--split", type=int, default=1, metavar="N",
                     help="split-KV parts per query tile (fa_fwd_split); 1 = fa_fwd")
     ap.add_argument("--bwd", action="store_true",
@@ -251,6 +254,17 @@ def main():
               "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     w = W.BY_NAME[args.workload]
+    if args.shape:
+        try:
+            dt, b, h, sq, sk, d, causal = args.shape.split(",")
+            b, h, sq, sk, d, causal = (int(x) for x in (b, h, sq, sk, d, causal))
+            if dt not in W.DTYPES or min(b, h, sq, sk, d) < 1 or causal not in (0, 1):
+                raise ValueError(args.shape)
+        except ValueError:
+            print("--shape wants DT,B,H,SQ,SK,D,CAUSAL with DT in %s" % (W.DTYPES,), file=sys.stderr)
+            sys.exit(2)
+        w = W.shape("shape_%s_b%dh%ds%dk%dd%d%s" % (dt, b, h, sq, sk, d, "_causal" if causal else ""),
+                    dt, b, h, sq, sk, d, bool(causal))
     if args.bwd and args.split > 1:
         print("--bwd and --split are exclusive", file=sys.stderr)
         sys.exit(2)

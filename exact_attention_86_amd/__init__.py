@@ -67,6 +67,8 @@ def lib() -> ctypes.CDLL:
         ip = ctypes.POINTER(ctypes.c_int)
         L.fa_query_config.argtypes = [ctypes.c_int, i64, ctypes.c_int, i64, i64, i64, i64, ip, ip, ip, ip]
         L.fa_query_config.restype = ctypes.c_int
+        L.fa_query_launch.argtypes = [ctypes.c_int, i64, ctypes.c_int, i64, i64, i64, i64, ip, ip]
+        L.fa_query_launch.restype = ctypes.c_int
         L.fa_last_error.argtypes = []
         L.fa_last_error.restype = ctypes.c_char_p
         L.fa_version.argtypes = []
@@ -112,6 +114,18 @@ def fa_query_config(dtype: int, d: int, causal: int = 0, b: int = 1, h: int = 1,
     if rc != FA_OK:
         raise FaError(rc, fa_last_error())
     return dict(zip(("block_m", "block_n", "waves", "lds"), (x.value for x in vals)))
+
+
+def fa_query_launch(dtype: int, d: int, causal: int = 0, b: int = 1, h: int = 1, sq: int = 1,
+                    sk: int = 1) -> dict:
+    """The grid fa_fwd launches on the current device, and whether it is the
+    persistent schedule."""
+    vals = [ctypes.c_int(0) for _ in range(2)]
+    rc = lib().fa_query_launch(int(dtype), int(d), int(causal), int(b), int(h), int(sq), int(sk),
+                               *[ctypes.byref(x) for x in vals])
+    if rc != FA_OK:
+        raise FaError(rc, fa_last_error())
+    return {"grid": vals[0].value, "persistent": bool(vals[1].value)}
 
 
 def fa_fwd(q, k, v, o, lse, b, h, sq, sk, d, scale, causal, dtype, stream) -> int:

@@ -71,6 +71,31 @@ __device__ __forceinline__ int item_tiles(const Params& p, int item, int (&mt)[2
     return mt[0] == mt[1] ? 1 : 2;
 }
 
+// Persistent schedule: the grid is G workgroups (about one per CU, G a
+// multiple of the XCD count) and each loops over work units, one unit = one
+// query tile (bh, mt).  Units are numbered level-major in cost order: unit t
+// is head t mod (b*h) at level t / (b*h), the heaviest causal tiles (the most
+// key tiles) first; without the causal mask every level costs the same.  Slot
+// s of XCD x (workgroup 8s + x) takes, in round r, unit r*G + 8*s' + x with
+// s' = s in even rounds and S-1-s in odd ones (S = G/8 slots per XCD): this
+// snake order gives the slot that drew one of the heaviest units of a round
+// one of the lightest of the next, so every slot ends up with about the same
+// number of key tiles without atomics or a workspace.  Unit t runs on XCD
+// t mod 8, so when b*h is a multiple of 8 every tile of a head runs on one
+// XCD and its L2 serves that head's K/V to all of them.
+__device__ __forceinline__ bool persist_unit(const Params& p, int r, int& bh, int& mt)
+{
+    const int G = gridDim.x, S = G / kXcds;
+    const int x = blockIdx.x % kXcds, s = blockIdx.x / kXcds;
+    const int s2 = (r & 1) ? S - 1 - s : s;
+    const long long t = (long long)r * G + (long long)s2 * kXcds + x;
+    if (t >= p.n_items) return false;
+    const int level = (int)(t / p.bh);
+    bh = (int)(t - (long long)level * p.bh);
+    mt = p.causal ? p.n_mtiles - 1 - level : level;
+    return true;
+}
+
 // ---------------------------------------------------------------------------
 // 16-bit kernel (fp16 / bf16 on the 32x32x16 matrix cores)
 // ---------------------------------------------------------------------------
@@ -81,8 +106,17 @@ __device__ __forceinline__ int item_tiles(const Params& p, int item, int (&mt)[2
 // consecutive rows at one logical chunk) is conflict-free when the 16 rows map
 // to 16 distinct 16-byte bank groups: a bijection on the low four row bits
 // (three bits for 128-byte rows, whose row parity already picks the half of a
-// 256-byte bank line).  The V tile is read with 8-byte transpose reads, for
-// which the 8-row swizzle below measured fastest.
+// 256-byte bank line).
+// The V tile is read with 8-byte transpose reads: 32 lanes (256 bytes) are
+// served per clock, and lanes 0-31 read 4 consecutive rows at the 4 logical
+// chunks of one 64-byte column group.  Rows of 256 bytes or more therefore
+// put row bits 0-1 on chunk bits 2-3 (the 4 rows land in 4 different 64-byte
+// quarters of the bank line) and row bit 2 on chunk bit 1: conflict-free, where
+// a 3-bit swizzle leaves a 2-way conflict (measured with the LDS bank-conflict
+// counter: 12 % of the kernel's time stalled before, none after).  That
+// swizzle is used for 256-byte rows (d = 128); other row lengths keep the
+// 3-bit form, whose read offsets need half the registers (the d = 256 kernel
+// has none to spare: the 4-bit form spilled more and ran slower there).
 template <int CPR>
 __device__ __forceinline__ int swz_k(int row)
 {
@@ -90,7 +124,27 @@ __device__ __forceinline__ int swz_k(int row)
         return ((row & 1) ? 8 : 0) ^ ((row & 2) ? 2 : 0) ^ ((row & 4) ? 1 : 0) ^ ((row & 8) ? 4 : 0);
     return ((row & 2) ? 4 : 0) ^ ((row & 4) ? 1 : 0) ^ ((row & 8) ? 2 : 0);
 }
-__device__ __forceinline__ int swz_v(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+template <int CPR>
+__device__ __forceinline__ int swz_v(int row)
+{
+    if (CPR == 16) return ((row & 3) << 2) | (((row >> 2) & 1) << 1);
+    return ((row & 3) << 1) | ((row >> 2) & 1);
+}
+// V transpose reads: NRV per-lane byte offsets (within the V tile, before the
+// 16-key step); d tile dt reads at offset rv[dt % NRV] + (dt / NRV) * VSTEP.
+// With the 4-bit swizzle every d tile of a 256-byte row has its own offset;
+// with the 3-bit one, d tiles two apart differ by 128 bytes (chunk bit 3,
+// which that swizzle does not touch).
+template <int CPR>
+struct VRead {
+    static constexpr int NRV = CPR == 16 ? 4 : 2;
+    static constexpr int VSTEP = CPR == 16 ? 256 : 128;
+    static __device__ __forceinline__ uint32_t offset(int e, int v_row, int vhalf, int vc)
+    {
+        const int logical = (e & 1) * 4 + 2 * vhalf + (vc >> 1) + 8 * ((e >> 1) & 1);
+        return v_row * CPR * 16 + ((logical ^ swz_v<CPR>(v_row)) << 4) + (vc & 1) * 8;
+    }
+};
 
 
 // QB 32-row query blocks per wave: every K or V operand read from LDS feeds
@@ -168,7 +222,7 @@ fa_fwd_16(Params p)
         const int cc = (w * DMA + j) * 64 + lane;
         const int row = cc / CPR, pch = cc % CPR;
         dk[j] = row * RB + ((pch ^ swz_k<CPR>(row)) << 4);
-        dv[j] = row * RB + ((pch ^ swz_v(row)) << 4);
+        dv[j] = row * RB + ((pch ^ swz_v<CPR>(row)) << 4);
     }
     const uint32_t lds0 = lds_addr(&lds[0][0][0]);
     // copy j of K or V for the tile at n0 into stage `stage`.  full: the tile
@@ -198,7 +252,7 @@ fa_fwd_16(Params p)
         } else {
             const int cc = (w * DMA + J) * 64 + lane;
             const int row = cc / CPR, pch = cc % CPR;
-            copy_1k<ST * 2 * TB + TB + J * 1024>(src, min(row, sk - 1 - n0) * RB + ((pch ^ swz_v(row)) << 4), lbase);
+            copy_1k<ST * 2 * TB + TB + J * 1024>(src, min(row, sk - 1 - n0) * RB + ((pch ^ swz_v<CPR>(row)) << 4), lbase);
         }
     };
     auto issue_tile = [&](auto st_tag, int n0) {
@@ -223,10 +277,10 @@ fa_fwd_16(Params p)
     //  reads key row 16kc + 8j + 4g + r, d = 32dt + 16*half + 4c
     const int sub = lane & 15, vr = sub >> 2, vc = sub & 3, vhalf = (lane >> 4) & 1;
     const int v_row = 4 * g + vr;
-    uint32_t rv[2];
+    constexpr int NRV = VRead<CPR>::NRV < NDT ? VRead<CPR>::NRV : NDT;
+    uint32_t rv[NRV];
 #pragma unroll
-    for (int e = 0; e < 2; ++e)
-        rv[e] = TB + v_row * RB + (((e * 4 + 2 * vhalf + (vc >> 1)) ^ swz_v(v_row)) << 4) + (vc & 1) * 8;
+    for (int e = 0; e < NRV; ++e) rv[e] = TB + VRead<CPR>::offset(e, v_row, vhalf, vc);
 
     auto process = [&](const int mt, const int split) {
         const int q0 = mt * BM;
@@ -395,7 +449,7 @@ fa_fwd_16(Params p)
             for (int kc = 0; kc < 2 * NKB; ++kc) {
 #pragma unroll
                 for (int dt = 0; dt < NDT; ++dt) {
-                    const char* va = sb + rv[dt & 1] + (dt >> 1) * 128 + kc * 16 * RB;
+                    const char* va = sb + rv[dt % NRV] + (dt / NRV) * VRead<CPR>::VSTEP + kc * 16 * RB;
                     const v4i16_t x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(va));
                     const v4i16_t x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(va + 8 * RB));
                     const u32x4_t a = u32x4_t{__builtin_bit_cast(u32x2_t, x0)[0], __builtin_bit_cast(u32x2_t, x0)[1],
@@ -521,7 +575,7 @@ fa_fwd_16(Params p)
 // the barrier that ends it.  Group A's wave i owns query
 // rows [64i, 64i+32) of the 256-row tile and group B's wave i rows
 // [64i+32, 64i+64), so both groups reach the causal diagonal together.
-template <int D, int BN, bool BF16, bool CAUSAL>
+template <int D, int BN, bool BF16, bool CAUSAL, bool PERSIST>
 __global__ void __launch_bounds__(512, 1)
 fa_fwd_16pp(Params p)
 {
@@ -544,8 +598,10 @@ fa_fwd_16pp(Params p)
     // [0..1] K stages, [2..3] V stages; BN rows x D, swizzled 16-byte chunks
     __shared__ __attribute__((aligned(16))) uint16_t lds[4][TILE];
 
-    int bh, item;
-    if (!map_item(p, bh, item)) return;
+    int bh = 0, item = 0;
+    if constexpr (!PERSIST) {
+        if (!map_item(p, bh, item)) return;
+    }
 
     const int tid = threadIdx.x;
     const int w = tid >> 6;
@@ -559,10 +615,17 @@ fa_fwd_16pp(Params p)
     constexpr float kRescaleThreshold = 8.f;
     constexpr float kRescaleLimit = 256.f;
 
-    const uint16_t* __restrict__ Q = (const uint16_t*)p.q + (size_t)bh * sq * D;
-    const uint16_t* __restrict__ K = (const uint16_t*)p.k + (size_t)bh * sk * D;
-    const uint16_t* __restrict__ V = (const uint16_t*)p.v + (size_t)bh * sk * D;
-    uint16_t* __restrict__ O = (uint16_t*)p.o + (size_t)bh * sq * D;
+    // this head's slices (set per work unit)
+    const uint16_t* __restrict__ Q = nullptr;
+    const uint16_t* __restrict__ K = nullptr;
+    const uint16_t* __restrict__ V = nullptr;
+    uint16_t* __restrict__ O = nullptr;
+    auto set_head = [&](int h) {
+        Q = (const uint16_t*)p.q + (size_t)h * sq * D;
+        K = (const uint16_t*)p.k + (size_t)h * sk * D;
+        V = (const uint16_t*)p.v + (size_t)h * sk * D;
+        O = (uint16_t*)p.o + (size_t)h * sq * D;
+    };
 
     // ---- copies: wave w fills LDS chunks (w*DMA + j)*64 + lane of a tile ----
     uint32_t dk[DMA], dv[DMA];
@@ -571,7 +634,7 @@ fa_fwd_16pp(Params p)
         const int cc = (w * DMA + j) * 64 + lane;
         const int row = cc / CPR, pch = cc % CPR;
         dk[j] = row * RB + ((pch ^ swz_k<CPR>(row)) << 4);
-        dv[j] = row * RB + ((pch ^ swz_v(row)) << 4);
+        dv[j] = row * RB + ((pch ^ swz_v<CPR>(row)) << 4);
     }
     const uint32_t lbase = __builtin_amdgcn_readfirstlane(lds_addr(&lds[0][0]) + w * DMA * 1024);
     auto copy_k = [&](auto j_tag, auto st_tag, int n0, bool full) {
@@ -593,7 +656,7 @@ fa_fwd_16pp(Params p)
         } else {
             const int cc = (w * DMA + J) * 64 + lane;
             const int row = cc / CPR, pch = cc % CPR;
-            copy_1k<(2 + ST) * TB + J * 1024>(src, min(row, sk - 1 - n0) * RB + ((pch ^ swz_v(row)) << 4), lbase);
+            copy_1k<(2 + ST) * TB + J * 1024>(src, min(row, sk - 1 - n0) * RB + ((pch ^ swz_v<CPR>(row)) << 4), lbase);
         }
     };
 
@@ -603,10 +666,10 @@ fa_fwd_16pp(Params p)
     for (int kk = 0; kk < NKR; ++kk) rk[kk] = l32 * RB + (((2 * kk + g) ^ swz_k<CPR>(l32)) << 4);
     const int sub = lane & 15, vr = sub >> 2, vc = sub & 3, vhalf = (lane >> 4) & 1;
     const int v_row = 4 * g + vr;
-    uint32_t rv[2];
+    static_assert(VRead<CPR>::NRV == NDT, "one read offset per d tile");
+    uint32_t rv[NDT];
 #pragma unroll
-    for (int e = 0; e < 2; ++e)
-        rv[e] = v_row * RB + (((e * 4 + 2 * vhalf + (vc >> 1)) ^ swz_v(v_row)) << 4) + (vc & 1) * 8;
+    for (int e = 0; e < NDT; ++e) rv[e] = VRead<CPR>::offset(e, v_row, vhalf, vc);
 
     auto process = [&](const int mt) {
         const int q0 = mt * BM;
@@ -660,7 +723,7 @@ fa_fwd_16pp(Params p)
                 for (int kc = 0; kc < 2 * NKB; ++kc)
 #pragma unroll
                     for (int dt = 0; dt < NDT; ++dt) {
-                        const char* va = vb_ + rv[dt & 1] + (dt >> 1) * 128 + kc * 16 * RB;
+                        const char* va = vb_ + rv[dt] + kc * 16 * RB;
                         const v4i16_t x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(va));
                         const v4i16_t x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(va + 8 * RB));
                         const u32x4_t a = u32x4_t{__builtin_bit_cast(u32x2_t, x0)[0], __builtin_bit_cast(u32x2_t, x0)[1],
@@ -680,7 +743,7 @@ fa_fwd_16pp(Params p)
                     constexpr int I = decltype(i_tag)::value;
                     if constexpr (I % 2 == 0) {
                         constexpr int op = I / 2, kc = op / NDT, dt = op % NDT;
-                        const char* va = vb_ + rv[dt & 1] + (dt >> 1) * 128 + kc * 16 * RB;
+                        const char* va = vb_ + rv[dt] + kc * 16 * RB;
                         const v4i16_t x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(va));
                         const v4i16_t x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(va + 8 * RB));
                         ring[I % kAhead] = u32x4_t{__builtin_bit_cast(u32x2_t, x0)[0], __builtin_bit_cast(u32x2_t, x0)[1],
@@ -836,12 +899,24 @@ fa_fwd_16pp(Params p)
         }
     };
 
-    int mts[2];
-    const int nt = item_tiles(p, item, mts);
-    process(mts[0]);
-    if (nt > 1) {
-        __syncthreads();  // every wave is done with the LDS stages
-        process(mts[1]);
+    if constexpr (PERSIST) {
+        // every wave computes the same unit, so the whole workgroup leaves together
+        for (int r = 0;; ++r) {
+            int mt;
+            if (!persist_unit(p, r, bh, mt)) break;
+            set_head(bh);
+            if (r > 0) __syncthreads();  // every wave is done with the LDS stages
+            process(mt);
+        }
+    } else {
+        set_head(bh);
+        int mts[2];
+        const int nt = item_tiles(p, item, mts);
+        process(mts[0]);
+        if (nt > 1) {
+            __syncthreads();  // every wave is done with the LDS stages
+            process(mts[1]);
+        }
     }
 }
 
@@ -1158,10 +1233,14 @@ static hipError_t launch16split(const Params& p, hipStream_t s)
 }
 
 template <int D, int BN, bool BF16>
-static hipError_t launch16pp(const Params& p, hipStream_t s)
+static hipError_t launch16pp(const Params& p, bool persist, hipStream_t s)
 {
-    if (p.causal) return launch(fa_fwd_16pp<D, BN, BF16, true>, 8, p, s);
-    return launch(fa_fwd_16pp<D, BN, BF16, false>, 8, p, s);
+    if (persist) {
+        if (p.causal) return launch(fa_fwd_16pp<D, BN, BF16, true, true>, 8, p, s);
+        return launch(fa_fwd_16pp<D, BN, BF16, false, true>, 8, p, s);
+    }
+    if (p.causal) return launch(fa_fwd_16pp<D, BN, BF16, true, false>, 8, p, s);
+    return launch(fa_fwd_16pp<D, BN, BF16, false, false>, 8, p, s);
 }
 
 template <int D, int BN, int NW>
@@ -1268,12 +1347,12 @@ hipError_t launch_fwd(int dtype, int d, const TileConfig& tc, const Params& p, h
     switch (dtype) {
     case 2:
         if (d == 64) return launch16<64, 128, 4, 1, true>(p, s);
-        if (d == 128) return tc.kind == 1 ? launch16pp<128, 64, true>(p, s) : launch16<128, 64, 4, 1, true>(p, s);
+        if (d == 128) return tc.kind ? launch16pp<128, 64, true>(p, tc.kind == 2, s) : launch16<128, 64, 4, 1, true>(p, s);
         if (d == 256) return launch16<256, 32, 4, 1, true>(p, s);
         break;
     case 1:
         if (d == 64) return launch16<64, 128, 4, 1, false>(p, s);
-        if (d == 128) return tc.kind == 1 ? launch16pp<128, 64, false>(p, s) : launch16<128, 64, 4, 1, false>(p, s);
+        if (d == 128) return tc.kind ? launch16pp<128, 64, false>(p, tc.kind == 2, s) : launch16<128, 64, 4, 1, false>(p, s);
         if (d == 256) return launch16<256, 32, 4, 1, false>(p, s);
         break;
     case 0:

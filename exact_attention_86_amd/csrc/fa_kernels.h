@@ -35,7 +35,8 @@ struct Params {
 struct TileConfig {
     int block_m, block_n, waves, lds;
     int qb;    // 32-row query blocks per wave
-    int kind;  // 0: one wave group; 1: two ping-pong wave groups
+    int kind;  // 0: one wave group; 1: two ping-pong wave groups, one workgroup per
+               // work item; 2: the same kernel on a persistent grid (fa_fwd sets it)
 };
 
 // Backward launch parameters (fa_bwd).

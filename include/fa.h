@@ -96,10 +96,34 @@ FA_API int fa_fwd(const void* q, const void* k, const void* v, void* o,
  *   lds      LDS bytes per workgroup
  * Any output pointer may be NULL.  Returns FA_OK, FA_ERR_INVALID_ARG (a size
  * below 1, causal not 0/1) or FA_ERR_UNSUPPORTED.  Host only; no HIP call.
+ * One function answers for both the launcher and its callers (tests, the
+ * benchmark), so the two cannot drift apart -- page "05 · kernel
+ * 工程与四代演化", section 7, warns of block-size tables kept in sync by hand
+ * in two places.
  */
 FA_API int fa_query_config(int dtype, int64_t d, int causal, int64_t b, int64_t h,
                            int64_t sq, int64_t sk, int* block_m, int* block_n,
                            int* waves, int* lds);
+
+/*
+ * fa_query_launch -- the grid fa_fwd launches for a problem on the current
+ * device (page "05 · kernel 工程与四代演化", section 4.3, describes the
+ * persistent tile scheduler: about one workgroup per compute unit claiming
+ * work items).
+ *   grid        workgroups launched
+ *   persistent  1: the 8-wave kernel runs on a persistent grid of about one
+ *               workgroup per CU that loops over single query tiles in cost
+ *               order (chosen for causal problems whose equal-cost pairs of
+ *               query tiles would leave the last round of workgroups mostly
+ *               empty); 0: one workgroup per work item (a causal pair of
+ *               query tiles, or one tile)
+ * Any output pointer may be NULL.  Asks the HIP runtime for the current
+ * device's compute-unit count (no launch, no allocation); without a device it
+ * reports the per-item grid.  Returns FA_OK, FA_ERR_INVALID_ARG,
+ * FA_ERR_UNSUPPORTED or FA_ERR_TOO_LARGE as fa_fwd would.
+ */
+FA_API int fa_query_launch(int dtype, int64_t d, int causal, int64_t b, int64_t h,
+                           int64_t sq, int64_t sk, int* grid, int* persistent);
 
 /*
  * fa_fwd_split -- the same forward with each query tile's key range cut into

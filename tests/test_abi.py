@@ -28,7 +28,7 @@ def declared_symbols():
 
 
 def test_header_declares_the_entry_points():
-    assert set(declared_symbols()) == {"fa_fwd", "fa_fwd_split", "fa_fwd_split_noalloc",
+    assert set(declared_symbols()) == {"fa_fwd", "fa_fwd_split", "fa_fwd_split_noalloc", "fa_query_launch",
                                        "fa_split_workspace_bytes",
                                        "fa_fwd_varlen", "fa_query_config", "fa_last_error",
                                        "fa_version", "fa_bwd", "fa_bwd_workspace_bytes",
@@ -414,3 +414,28 @@ def test_noalloc_invalid_arguments_rejected_before_launch(kw, code):
     args.update(kw)
     assert fa.fa_fwd_split_noalloc(**args) == code
     assert fa.fa_last_error().startswith("fa_fwd")
+
+
+# ---- fa_query_launch ----
+def test_query_launch_per_item_grid_without_a_device():
+    # causal pairs of 256-row tiles: 4*32 heads x 8 pairs, grid rounded up to the 8 XCDs
+    r = fa.fa_query_launch(fa.FA_BF16, 128, 1, 4, 32, 4096, 4096)
+    assert r["grid"] == 1024
+    r = fa.fa_query_launch(fa.FA_F16, 128, 0, 1, 3, 100, 100)  # 4-wave kernel, one 128-row tile per head
+    assert r == {"grid": 8, "persistent": False}
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(b=0), fa.FA_ERR_INVALID_ARG),
+    (dict(sq=0), fa.FA_ERR_INVALID_ARG),
+    (dict(causal=2), fa.FA_ERR_INVALID_ARG),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=7), fa.FA_ERR_UNSUPPORTED),
+    (dict(b=1 << 20, h=1 << 12, sq=1 << 10), fa.FA_ERR_TOO_LARGE),
+])
+def test_query_launch_rejects(kw, code):
+    args = dict(dtype=fa.FA_BF16, d=128, causal=1, b=1, h=1, sq=64, sk=64)
+    args.update(kw)
+    with pytest.raises(fa.FaError) as e:
+        fa.fa_query_launch(**args)
+    assert e.value.code == code

@@ -25,7 +25,9 @@ def test_more_than_one_gpu_is_refused_with_a_message():
 
 
 @pytest.mark.parametrize("args", [["--bwd", "--split", "4"], ["--fp8", "--bwd"],
-                                  ["--fp8", "--workload", "tiny_fp32_b1h2s128d64"]])
+                                  ["--fp8", "--workload", "tiny_fp32_b1h2s128d64"],
+                                  ["--shape", "bf16,1,2,3"], ["--shape", "q8,1,1,64,64,128,0"],
+                                  ["--shape", "bf16,1,1,64,64,128,2"]])
 def test_exclusive_options_are_refused_before_any_device_call(args):
     r = run_bench(*args)
     assert r.returncode == 2, r.stderr

@@ -173,6 +173,32 @@ def test_pingpong_shapes_full_compare(case, gpu):
     compare_full(W.shape("pp", dt, b, h, sq, sk, d, causal, seed=sq + sk))
 
 
+# causal problems whose pairs of query tiles would leave the last round of
+# workgroups mostly empty run the 8-wave kernel on the persistent grid
+PERSISTENT = [
+    ("bf16", 1, 300, 1000, 1000, True),     # 600 pairs on 256 CUs
+    ("f16", 1, 260, 700, 650, True),        # causal sq > sk, ragged
+    ("bf16", 2, 150, 1300, 1300, True),     # ragged last tile
+]
+
+
+@pytest.mark.parametrize("case", PERSISTENT, ids=lambda c: "%s-b%dh%d-sq%d-sk%d" % c[:5])
+def test_persistent_schedule_full_compare(case, gpu):
+    dt, b, h, sq, sk, causal = case
+    launch = fa.fa_query_launch(W.DTYPE_CODE[dt], 128, int(causal), b, h, sq, sk)
+    note(f"  launch {launch}")
+    assert launch["persistent"] and launch["grid"] % 8 == 0
+    compare_full(W.shape("persist", dt, b, h, sq, sk, 128, causal, seed=sq + 2 * sk))
+
+
+def test_benchmark_shapes_use_the_per_item_grid(gpu):
+    """The rule keeps the head-major per-item grid where pairs fill whole
+    rounds (the headline and the 16k workloads)."""
+    for w in (W.WORKLOADS[2], W.WORKLOADS[3]):
+        launch = fa.fa_query_launch(W.DTYPE_CODE[w.dtype], w.d, int(w.causal), w.b, w.h, w.sq, w.sk)
+        assert not launch["persistent"], (w.name, launch)
+
+
 @pytest.mark.parametrize("scale", [-0.125, 0.0, 0.5])
 def test_unusual_scales(scale, gpu):
     compare_full(W.shape("scale", "bf16", 1, 2, 100, 130, 128, True, scale=scale, seed=3))
@@ -230,11 +256,12 @@ def test_one_hot_wide_score_range(dt, d, sk, gpu):
     assert float(np.abs(lse[0, 0].double().cpu().numpy() - (64.0 + np.log(cnt))).max()) <= TOL_LSE
 
 
-@pytest.mark.parametrize("b,h,sq,waves", [(2, 4, 777, 4), (1, 256, 4096, 8)])
+@pytest.mark.parametrize("b,h,sq,waves", [(2, 4, 777, 4), (1, 256, 4096, 8), (1, 300, 1000, 8)])
 def test_deterministic(b, h, sq, waves, gpu):
     """Two runs give the same bits, for the 4-wave kernel and for the 8-wave
     ping-pong kernel (which has no barrier between the two slots of a key
-    window, so a race on an LDS stage would show up as run-to-run noise)."""
+    window, so a race on an LDS stage would show up as run-to-run noise), on
+    its per-item and on its persistent grid."""
     import torch
     cfg = fa.fa_query_config(W.DTYPE_CODE["bf16"], 128, 1, b, h, sq, sq)
     assert cfg["waves"] == waves
@@ -247,7 +274,7 @@ def test_deterministic(b, h, sq, waves, gpu):
 
 
 @pytest.mark.parametrize("dt,h,sq,sk,causal", [("bf16", 256, 4096, 4096, True), ("f16", 256, 333, 200, True),
-                                              ("bf16", 300, 260, 390, False)])
+                                              ("bf16", 300, 260, 390, False), ("bf16", 300, 1000, 1000, True)])
 def test_eight_waves_equal_four_waves(dt, h, sq, sk, causal, gpu):
     """The same problem through the 8-wave ping-pong kernel (fa_fwd on many
     heads) and through the 4-wave kernel (fa_fwd_varlen with one sequence per
