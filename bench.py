@@ -79,78 +79,26 @@ def cpu_model() -> str:
     return "unknown"
 
 
-class ClockSampler:
-    """Samples the graphics (shader) clock of the GPU that runs the kernels,
-    in MHz, from amdsmi every ``period`` seconds in a background thread while
-    the timed launches run.  Reports None when amdsmi is unavailable or the
-    device cannot be matched."""
-
-    def __init__(self, torch_mod, period: float = 0.01):
-        import threading
-        self.samples = []
-        self.period = period
-        self.error = None
-        self._stop = threading.Event()
-        self._thread = None
-        self._handle = None
-        self._smi = None
-        try:
-            import amdsmi
-            amdsmi.amdsmi_init()
-            handles = amdsmi.amdsmi_get_processor_handles()
-            want = None
-            try:
-                props = torch_mod.cuda.get_device_properties(torch_mod.cuda.current_device())
-                want = int(getattr(props, "pci_bus_id"))
-            except Exception:  # noqa: BLE001 - older torch: no bus id
-                want = None
-            chosen = None
-            for h in handles:
-                bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)  # "dddd:bb:dd.f"
-                if want is not None and int(bdf.split(":")[1], 16) == want:
-                    chosen = h
-            if chosen is None and len(handles) == 1:
-                chosen = handles[0]
-            if chosen is None:
-                self.error = "device not matched among %d amdsmi handles" % len(handles)
-            else:
-                self._handle, self._smi = chosen, amdsmi
-                self.read()  # fails here, not in the thread, if clocks are not readable
-        except Exception as e:  # noqa: BLE001 - report, never fail the bench
-            self.error = "amdsmi: %s" % e
-            self._handle = None
-
-    def read(self) -> float:
-        info = self._smi.amdsmi_get_clock_info(self._handle, self._smi.AmdSmiClkType.GFX)
-        return float(info["clk"])
-
-    def _run(self):
-        while not self._stop.wait(self.period):
-            try:
-                self.samples.append(self.read())
-            except Exception as e:  # noqa: BLE001
-                self.error = "amdsmi: %s" % e
-                return
-
-    def start(self):
-        if self._handle is not None:
-            import threading
-            self._thread = threading.Thread(target=self._run, daemon=True)
-            self._thread.start()
-
-    def stop(self):
-        if self._thread is not None:
-            self._stop.set()
-            self._thread.join()
-
-    def summary(self):
-        if not self.samples:
-            return {"mhz_median": None, "samples": 0, "source": "amdsmi GFX clock",
-                    "error": self.error}
-        s = sorted(self.samples)
-        return {"mhz_median": s[len(s) // 2], "mhz_min": s[0], "mhz_max": s[-1],
-                "samples": len(s), "source": "amdsmi GFX clock, sampled every %.0f ms during the "
-                "timed launches" % (self.period * 1e3)}
+def shader_clock(torch_mod, fa_mod, step, stream, n: int = 24, ticks: int = 2000):
+    """Shader clock the kernels ran at, in MHz: after the timed region, n more
+    steps each followed on the same stream by fa_clock_probe (one wave counts
+    shader-clock cycles over `ticks` ticks of the 100 MHz real-time counter).
+    The power manager sets the clock on a millisecond scale, so a probe right
+    behind a launch sees that launch's clock.  The probe lands on one XCD; the
+    rocprofv3 summaries give the all-XCD figure (GRBM_GUI_ACTIVE per XCD over
+    the kernel duration)."""
+    buf = torch_mod.zeros(2 * n, dtype=torch_mod.int64, device="cuda")
+    for i in range(n):
+        step()
+        rc = fa_mod.lib().fa_clock_probe(buf.data_ptr() + 16 * i, ticks, stream.cuda_stream)
+        if rc != fa_mod.FA_OK:
+            raise fa_mod.FaError(rc, fa_mod.fa_last_error())
+    torch_mod.cuda.synchronize()
+    mhz = sorted(c / r * 100.0 for c, r in buf.view(n, 2).cpu().tolist() if r > 0)
+    return {"mhz_median": round(mhz[len(mhz) // 2], 1), "mhz_min": round(mhz[0], 1),
+            "mhz_max": round(mhz[-1], 1), "samples": len(mhz),
+            "source": "fa_clock_probe (s_memtime cycles over s_memrealtime 100 MHz ticks, "
+                      "%d us) right behind each of %d launches after the timed region" % (ticks // 100, n)}
 
 
 def kernel_sha() -> str:
@@ -352,12 +300,9 @@ def main():
             torch.cuda.synchronize()
     torch.cuda.synchronize()
 
-    # per-launch kernel time: HIP events on the launch stream around each call;
-    # the shader clock is sampled alongside
-    clock = ClockSampler(torch)
+    # per-launch kernel time: HIP events on the launch stream around each call
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
-    clock.start()
     t0 = time.perf_counter()
     evs[0].record(stream)
     for i in range(args.steps):
@@ -365,7 +310,7 @@ def main():
         evs[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    clock.stop()
+    sclk = shader_clock(torch, fa, step, stream)
     per = [evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)]
     avg_ms = sum(per) / len(per)
     med_ms = sorted(per)[len(per) // 2]
@@ -376,13 +321,12 @@ def main():
     achieved = flops / (avg_ms * 1e-3) / 1e12
     dtype = "fp8_e4m3" if args.fp8 else w.dtype
     peak = PEAK_TFLOPS[dtype]
-    log("[bench] shader clock: %s" % clock.summary())
+    log("[bench] shader clock: %s" % sclk)
     log("[bench] %s: wall %.3f ms/step, kernel avg %.3f ms (min %.3f, max %.3f), "
         "%.1f TFLOP/s = %.1f%% of %.1f; %.0f GB/s algorithmic" % (
             w.name, ms_per_step, avg_ms, min(per), max(per), achieved,
             100 * achieved / peak, peak, w.algorithmic_bytes / (avg_ms * 1e-3) / 1e9))
 
-    sclk = clock.summary()
     # the matrix peak scales with the shader clock: % of peak at the clock seen
     frac_sclk = None
     if sclk.get("mhz_median"):

@@ -93,6 +93,8 @@ def lib() -> ctypes.CDLL:
         L.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float,
                                  ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_int, vp]
         L.fa_fwd_fp8.restype = ctypes.c_int
+        L.fa_clock_probe.argtypes = [vp, i64, vp]
+        L.fa_clock_probe.restype = ctypes.c_int
         _lib = L
         return L
 

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfa.so")
-SOURCES = ["fa_api.cpp", "fa_fwd_kernels.hip", "fa_bwd_kernels.hip", "fa_fp8_kernels.hip"]
+SOURCES = ["fa_api.cpp", "fa_fwd_kernels.hip", "fa_bwd_kernels.hip", "fa_fp8_kernels.hip", "fa_probe.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

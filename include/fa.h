@@ -306,6 +306,22 @@ FA_API int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o,
                       int64_t d, float scale, float descale_q, float descale_k,
                       float descale_v, int causal, void* stream);
 
+/*
+ * fa_clock_probe -- measurement aid, not part of the attention path: reads
+ * the shader clock the GPU runs at.  One wave reads the shader-clock counter
+ * and the constant 100 MHz real-time counter, spins for `ticks` real-time
+ * ticks (10 ns each), and writes two values to `out` (device pointer, 2
+ * uint64, 8-byte aligned, caller-owned): out[0] = shader-clock cycles and
+ * out[1] = real-time ticks elapsed, so the clock is out[0] / out[1] * 100 MHz.
+ * Enqueued on `stream` right behind attention launches, it sees the clock the
+ * power manager chose for them.  The matrix-core peak is 4096 FLOP per clock
+ * per compute unit at 16 bits, so this clock turns a throughput into a
+ * fraction of the peak at the clock actually seen.
+ * Returns FA_OK, FA_ERR_INVALID_ARG (NULL, ticks outside [1, 10^7]),
+ * FA_ERR_MISALIGNED or FA_ERR_HIP.
+ */
+FA_API int fa_clock_probe(unsigned long long* out, int64_t ticks, void* stream);
+
 /* fa_last_error -- message of the last failing call on this host thread
  * ("" if none).  The pointer stays valid until the next call on the thread. */
 FA_API const char* fa_last_error(void);

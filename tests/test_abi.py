@@ -32,7 +32,7 @@ def test_header_declares_the_entry_points():
                                        "fa_split_workspace_bytes",
                                        "fa_fwd_varlen", "fa_query_config", "fa_last_error",
                                        "fa_version", "fa_bwd", "fa_bwd_workspace_bytes",
-                                       "fa_fwd_fp8"}
+                                       "fa_fwd_fp8", "fa_clock_probe"}
 
 
 def test_library_loads_and_exports_every_declared_symbol():
@@ -439,3 +439,12 @@ def test_query_launch_rejects(kw, code):
     with pytest.raises(fa.FaError) as e:
         fa.fa_query_launch(**args)
     assert e.value.code == code
+
+
+def test_clock_probe_argument_checks():
+    # every rejection happens on the host, before any HIP call
+    L_ = fa.lib()
+    assert L_.fa_clock_probe(None, 2000, None) == fa.FA_ERR_INVALID_ARG
+    assert L_.fa_clock_probe(A, 0, None) == fa.FA_ERR_INVALID_ARG
+    assert L_.fa_clock_probe(A, 10000001, None) == fa.FA_ERR_INVALID_ARG
+    assert L_.fa_clock_probe(A + 4, 2000, None) == fa.FA_ERR_MISALIGNED
