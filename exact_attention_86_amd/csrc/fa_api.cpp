@@ -462,7 +462,10 @@ FA_API int fa_bwd(const void* q, const void* k, const void* v, const void* o, co
     p.bh = (int)(b * h);
     p.sq = (int)sq;
     p.sk = (int)sk;
-    p.c = (float)((double)scale * 1.4426950408889634);
+    // signed exponent factor; a zero scale uses 1e-30 as the forward does
+    // (exp2(1e-30 s) is exactly 1 in fp32), so c is never zero and a masked
+    // score of -inf * sign(c) always exponentiates to 0
+    p.c = scale != 0.f ? (float)((double)scale * 1.4426950408889634) : 1e-30f;
     p.scale = scale;
     p.causal = causal;
     p.items_per_head = 0;

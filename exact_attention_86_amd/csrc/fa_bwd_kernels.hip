@@ -131,6 +131,7 @@ fa_bwd_dkdv(BwdParams p)
     const int sq = p.sq, sk = p.sk;
     const int n0 = kt * BN;
     const float c = p.c;
+    const uint32_t dead_bits = c > 0.f ? 0xff800000u : 0x7f800000u;  // -inf * sign(c)
 
     const uint16_t* __restrict__ Q = (const uint16_t*)p.q + (size_t)bh * sq * D;
     const uint16_t* __restrict__ dO = (const uint16_t*)p.dout + (size_t)bh * sq * D;
@@ -270,7 +271,25 @@ fa_bwd_dkdv(BwdParams p)
                 l4[rb] = *(const f32x4_t*)(sb + OFF_LSE + (32 * qb + 8 * rb + 4 * g) * 4);
                 d4[rb] = *(const f32x4_t*)(sb + OFF_D + (32 * qb + 8 * rb + 4 * g) * 4);
             }
+            // masks (diagonal and ragged blocks only, a wave-uniform branch
+            // around one pass): score rr belongs to query qbase + 4g + off(rr)
+            // and lives iff key <= query < sq; dead scores become -inf * sign(c)
+            // (c is never zero), so their probability and dS are exactly 0.
+            // The select is a sign mask and a bit-field insert, one pass before
+            // the exponentials.
             const bool need_mask = (qbase + 32 > sq) || (CAUSAL && qbase < n0 + 32 * w + 31);
+            if (need_mask) {
+                const int lo = CAUSAL ? key - qbase - 4 * g : -(1 << 20);
+                const int hi1 = sq - qbase - 4 * g - 1;
+#pragma unroll
+                for (int rr = 0; rr < 16; ++rr) {
+                    const int off = (rr >> 2) * 8 + (rr & 3);
+                    const uint32_t dead = (uint32_t)(((off - lo) | (hi1 - off)) >> 31);
+                    const float x = s[rr];  // through a scalar: a bit cast of a vector element reads element 0
+                    const uint32_t bits = __builtin_bit_cast(uint32_t, x);
+                    s[rr] = __builtin_bit_cast(float, (bits & ~dead) | (dead_bits & dead));
+                }
+            }
             u32x4_t pp[2], dsp[2];
 #pragma unroll
             for (int r = 0; r < 16; r += 2) {
@@ -278,11 +297,7 @@ fa_bwd_dkdv(BwdParams p)
 #pragma unroll
                 for (int e = 0; e < 2; ++e) {
                     const int rr = r + e;
-                    float pv = fast_exp2(__builtin_fmaf(s[rr], c, -l4[rr >> 2][rr & 3]));
-                    if (need_mask) {
-                        const int query = qbase + (rr >> 2) * 8 + 4 * g + (rr & 3);
-                        if (query >= sq || (CAUSAL && key > query)) pv = 0.f;
-                    }
+                    const float pv = fast_exp2(__builtin_fmaf(s[rr], c, -l4[rr >> 2][rr & 3]));
                     pr[e] = pv;
                     dr[e] = pv * (dp[rr] - d4[rr >> 2][rr & 3]);
                 }
@@ -372,6 +387,7 @@ fa_bwd_dq(BwdParams p)
     const int g = lane >> 5;
     const int sq = p.sq, sk = p.sk;
     const float c = p.c;
+    const uint32_t dead_bits = c > 0.f ? 0xff800000u : 0x7f800000u;  // -inf * sign(c)
     const int mt = CAUSAL ? p.items_per_head - 1 - item : item;  // causal: heaviest tiles first
     const int q0 = mt * BM;
 
@@ -468,8 +484,23 @@ fa_bwd_dq(BwdParams p)
                 dp = mfma16(av, gf[kk], dp, BF16);
             }
 
-            // ---- dS^T = P^T (dP^T - D); row r holds key 8(r/4) + 4g + r%4 ----
+            // ---- dS^T = P^T (dP^T - D); row r holds key 8(r/4) + 4g + r%4.
+            //      Masks (diagonal and ragged blocks only, one pass before the
+            //      exponentials): key kbase + 4g + off(r) lives iff it is below
+            //      min(sk, qrow + 1) when causal, else below sk; a dead score
+            //      becomes -inf * sign(c), so its probability is exactly 0 ----
             const bool need_mask = (kbase + 32 > sk) || (CAUSAL && kbase + 31 > wq);
+            if (need_mask) {
+                const int lim = (CAUSAL ? min(sk, qrow + 1) : sk) - kbase - 4 * g - 1;
+#pragma unroll
+                for (int rr = 0; rr < 16; ++rr) {
+                    const int off = (rr >> 2) * 8 + (rr & 3);
+                    const uint32_t dead = (uint32_t)((lim - off) >> 31);
+                    const float x = s[rr];  // through a scalar: a bit cast of a vector element reads element 0
+                    const uint32_t bits = __builtin_bit_cast(uint32_t, x);
+                    s[rr] = __builtin_bit_cast(float, (bits & ~dead) | (dead_bits & dead));
+                }
+            }
             u32x4_t dsp[2];
 #pragma unroll
             for (int r = 0; r < 16; r += 2) {
@@ -477,11 +508,7 @@ fa_bwd_dq(BwdParams p)
 #pragma unroll
                 for (int e = 0; e < 2; ++e) {
                     const int rr = r + e;
-                    float pv = fast_exp2(__builtin_fmaf(s[rr], c, -lse2));
-                    if (need_mask) {
-                        const int kidx = kbase + (rr >> 2) * 8 + 4 * g + (rr & 3);
-                        if (kidx >= sk || (CAUSAL && kidx > qrow)) pv = 0.f;
-                    }
+                    const float pv = fast_exp2(__builtin_fmaf(s[rr], c, -lse2));
                     dr[e] = pv * (dp[rr] - drow);
                 }
                 dsp[r >> 3][(r >> 1) & 3] = pack2(dr[0], dr[1], BF16);
