@@ -168,6 +168,16 @@ fa_bwd_dkdv(BwdParams p)
         const int row = cc >> 4, pch = cc & 15;
         cof[j] = row * RB + ((pch ^ swz_b(row)) << 4);
     }
+    // copy C (0..2*DMA-1: Q copies, then dO copies) of the tile at query q0
+    // into stage ST; rows past the last query re-read it (masked later), by
+    // arithmetic, so a copy is one branch-free instruction
+    auto copy_one = [&](auto st_tag, auto c_tag, int q0) {
+        constexpr int ST = decltype(st_tag)::value, C = decltype(c_tag)::value, J = C % DMA;
+        const int row = ((w * DMA + J) * 64 + lane) >> 4;
+        const uint32_t off = cof[J] - (uint32_t)(max(row - (sq - 1 - q0), 0) * RB);
+        const void* src = uniform_ptr((C < DMA ? Q : dO) + (size_t)q0 * D);
+        copy_1k<ST * STAGE + (C < DMA ? 0 : TQ) + J * 1024>(src, off, lbase);
+    };
     auto issue = [&](auto st_tag, int q0) {
         constexpr int ST = decltype(st_tag)::value;
         const bool full = q0 + BMQ <= sq;
@@ -225,94 +235,219 @@ fa_bwd_dkdv(BwdParams p)
             dka[dt][r] = 0.f;
         }
 
-    auto compute = [&](auto st_tag, int q0) {
+    // One 32-query block (qb = 0, 1 of the stage) in three pieces, so that
+    // two blocks can be interleaved: the score products, the softmax, and
+    // the dV and dK products.
+    // block_mask: the causal and ragged masks of a block's scores as one pass
+    // (diagonal and ragged blocks only): score rr belongs to query qbase + 4g
+    // + off(rr) and lives iff key <= query < sq; a dead score becomes
+    // -inf * sign(c) (c is never zero), so its probability and dS are exactly
+    // 0.  The select is a sign mask and a bit-field insert.
+    auto block_mask = [&](f32x16_t& s, int qbase) {
+        const bool need_mask = (qbase + 32 > sq) || (CAUSAL && qbase < n0 + 32 * w + 31);
+        if (need_mask) {
+            const int lo = CAUSAL ? key - qbase - 4 * g : -(1 << 20);
+            const int hi1 = sq - qbase - 4 * g - 1;
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) {
+                const int off = (rr >> 2) * 8 + (rr & 3);
+                const uint32_t dead = (uint32_t)(((off - lo) | (hi1 - off)) >> 31);
+                const float x = s[rr];  // through a scalar: a bit cast of a vector element reads element 0
+                const uint32_t bits = __builtin_bit_cast(uint32_t, x);
+                s[rr] = __builtin_bit_cast(float, (bits & ~dead) | (dead_bits & dead));
+            }
+        }
+    };
+    // the block's LSE (log2 units) and D: accumulator row r holds query
+    // 8(r/4) + 4g + r%4 of the block
+    auto block_rows = [&](const char* sb, int qb, f32x4_t (&l4)[4], f32x4_t (&d4)[4]) {
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+            l4[rb] = *(const f32x4_t*)(sb + OFF_LSE + (32 * qb + 8 * rb + 4 * g) * 4);
+            d4[rb] = *(const f32x4_t*)(sb + OFF_D + (32 * qb + 8 * rb + 4 * g) * 4);
+        }
+    };
+    // softmax element rr: P = exp2(c s - LSE log2 e), dS = P (dP - D); the
+    // pair (rr - 1, rr) is packed at odd rr
+    auto soft_el = [&](int rr, const f32x16_t& s, const f32x16_t& dp, const f32x4_t (&l4)[4],
+                       const f32x4_t (&d4)[4], float (&pr)[16], float (&dr)[16], u32x4_t (&pp)[2],
+                       u32x4_t (&dsp)[2]) {
+        pr[rr] = fast_exp2(__builtin_fmaf(s[rr], c, -l4[rr >> 2][rr & 3]));
+        dr[rr] = pr[rr] * (dp[rr] - d4[rr >> 2][rr & 3]);
+        if (rr & 1) {
+            pp[rr >> 3][(rr >> 1) & 3] = pack2(pr[rr - 1], pr[rr], BF16);
+            dsp[rr >> 3][(rr >> 1) & 3] = pack2(dr[rr - 1], dr[rr], BF16);
+        }
+    };
+
+    // the simple form: the three pieces of one block one after another
+    auto compute_block = [&](const char* sb, int qb, int qbase) {
+        const char* qblk = sb + qb * 32 * RB;
+        f32x16_t s, dp;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            s[r] = 0.f;
+            dp[r] = 0.f;
+        }
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+            const u32x4_t aq = *(const u32x4_t*)(qblk + rq[kk]);
+            const u32x4_t ag = *(const u32x4_t*)(qblk + TQ + rq[kk]);
+            s = mfma16(aq, kf[kk], s, BF16);
+            dp = mfma16(ag, vf[kk], dp, BF16);
+        }
+        // the transposed dO and Q operands of the dV and dK products go out
+        // now, so their LDS latency hides behind the softmax
+        u32x4_t opg[2][NDT], opq[2][NDT];
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) {
+            const char* base = qblk + kc * 16 * RB;
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) {
+                opg[kc][dt] = tr_pair(base + TQ + rt[0][dt], base + TQ + rt[1][dt]);
+                opq[kc][dt] = tr_pair(base + rt[0][dt], base + rt[1][dt]);
+            }
+        }
+        f32x4_t l4[4], d4[4];
+        block_rows(sb, qb, l4, d4);
+        block_mask(s, qbase);
+        float pr[16], dr[16];
+        u32x4_t pp[2], dsp[2];
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) soft_el(rr, s, dp, l4, d4, pr, dr, pp, dsp);
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) {
+                dva[dt] = mfma16(opg[kc][dt], pp[kc], dva[dt], BF16);
+                dka[dt] = mfma16(opq[kc][dt], dsp[kc], dka[dt], BF16);
+            }
+    };
+
+    // A stage's two blocks.  When both are live they are interleaved:
+    // S/dP(0); S/dP(1) with the softmax of block 0; dV/dK(0) with the softmax
+    // of block 1; dV/dK(1).  One wave per SIMD, so the wave itself keeps its
+    // matrix cores busy while its softmax runs (one softmax element per
+    // matrix-core instruction).  Each stream's LDS operands come from a small
+    // register ring; the empty volatile asm statements pin the softmax results
+    // in place (otherwise the compiler sinks them to their first use and the
+    // overlap is lost).
+    // compute(S, q0, qn): the stage-S tile at q0; the copies of the tile at
+    // qn into stage S^1 go out during the matrix-core streams (qn = q0 on the
+    // last step: a harmless refill of a stage nobody reads again)
+    auto compute = [&](auto st_tag, int q0, int qn) {
         constexpr int S = decltype(st_tag)::value;
         const char* sb = lds + S * STAGE;
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-            const int qbase = q0 + 32 * qb;  // first query of this 32-row block
-            if (qbase >= sq) break;
-            if (CAUSAL && qbase + 31 < n0 + 32 * w) continue;  // all its queries precede this wave's keys
-            const char* qblk = sb + qb * 32 * RB;
-
-            // ---- S = Q K^T and dP = dO V^T: lane = key, rows = queries ----
-            f32x16_t s, dp;
+        const bool ok0 = q0 < sq && !(CAUSAL && q0 + 31 < n0 + 32 * w);
+        const bool ok1 = q0 + 32 < sq && !(CAUSAL && q0 + 63 < n0 + 32 * w);
+        // copy C goes out with matrix-core instruction I of stream X
+        auto copy_at = [&](auto x_tag, auto i_tag) {
+            constexpr int X = decltype(x_tag)::value, I = decltype(i_tag)::value;
+            constexpr int C = X == 0 ? (I == 2 ? 0 : I == 7 ? 1 : -1)
+                            : X == 1 ? (I == 2 ? 2 : I == 7 ? 3 : I == 12 ? 4 : -1)
+                                     : (I == 2 ? 5 : I == 7 ? 6 : I == 12 ? 7 : -1);
+            if constexpr (C >= 0 && C < 2 * DMA) copy_one(Stage<S ^ 1>{}, Stage<C>{}, qn);
+        };
+        static_assert(2 * DMA == 8, "eight copies per wave per step");
+        if (ok0 && ok1) {
+            constexpr int KA = 4;
+            // ---- S/dP of block 0 ----
+            f32x16_t s0, dp0, s1, dp1;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                s[r] = 0.f;
-                dp[r] = 0.f;
+                s0[r] = 0.f;
+                dp0[r] = 0.f;
             }
-#pragma unroll
-            for (int kk = 0; kk < NKK; ++kk) {
-                const u32x4_t aq = *(const u32x4_t*)(qblk + rq[kk]);
-                const u32x4_t ag = *(const u32x4_t*)(qblk + TQ + rq[kk]);
-                s = mfma16(aq, kf[kk], s, BF16);
-                dp = mfma16(ag, vf[kk], dp, BF16);
+            {
+                const char* qblk = sb;
+                u32x4_t ring[KA];
+                // instruction i: even -> S (Q fragment), odd -> dP (dO fragment), k-step i/2
+                auto fetch = [&](auto f_tag) {
+                    constexpr int F = decltype(f_tag)::value;
+                    ring[F % KA] = *(const u32x4_t*)(qblk + (F % 2 ? TQ : 0) + rq[F / 2]);
+                };
+                static_for<KA>([&](auto f) { fetch(f); });
+                static_for<2 * NKK>([&](auto i_tag) {
+                    constexpr int I = decltype(i_tag)::value;
+                    const u32x4_t a = ring[I % KA];
+                    if constexpr (I + KA < 2 * NKK) fetch(Stage<I + KA>{});
+                    if constexpr (I % 2 == 0) s0 = mfma16(a, kf[I / 2], s0, BF16);
+                    else dp0 = mfma16(a, vf[I / 2], dp0, BF16);
+                    copy_at(Stage<0>{}, Stage<I>{});
+                    __builtin_amdgcn_sched_barrier(0);
+                });
             }
-
-            // ---- the transposed dO and Q operands of the dV and dK products
-            //      go out now, so their LDS latency hides behind the softmax ----
-            u32x4_t opg[2][NDT], opq[2][NDT];
+            // ---- S/dP of block 1 with the softmax of block 0 ----
+            f32x4_t l40[4], d40[4];
+            block_rows(sb, 0, l40, d40);
+            block_mask(s0, q0);
+            float pr0[16], dr0[16];
+            u32x4_t pp0[2], dsp0[2];
 #pragma unroll
-            for (int kc = 0; kc < 2; ++kc) {
-                const char* base = qblk + kc * 16 * RB;
-#pragma unroll
-                for (int dt = 0; dt < NDT; ++dt) {
-                    opg[kc][dt] = tr_pair(base + TQ + rt[0][dt], base + TQ + rt[1][dt]);
-                    opq[kc][dt] = tr_pair(base + rt[0][dt], base + rt[1][dt]);
+            for (int r = 0; r < 16; ++r) {
+                s1[r] = 0.f;
+                dp1[r] = 0.f;
+            }
+            {
+                const char* qblk = sb + 32 * RB;
+                u32x4_t ring[KA];
+                auto fetch = [&](auto f_tag) {
+                    constexpr int F = decltype(f_tag)::value;
+                    ring[F % KA] = *(const u32x4_t*)(qblk + (F % 2 ? TQ : 0) + rq[F / 2]);
+                };
+                static_for<KA>([&](auto f) { fetch(f); });
+                static_for<2 * NKK>([&](auto i_tag) {
+                    constexpr int I = decltype(i_tag)::value;
+                    const u32x4_t a = ring[I % KA];
+                    if constexpr (I + KA < 2 * NKK) fetch(Stage<I + KA>{});
+                    if constexpr (I % 2 == 0) s1 = mfma16(a, kf[I / 2], s1, BF16);
+                    else dp1 = mfma16(a, vf[I / 2], dp1, BF16);
+                    soft_el(I, s0, dp0, l40, d40, pr0, dr0, pp0, dsp0);
+                    asm volatile("" : "+v"(pr0[I]), "+v"(dr0[I]));
+                    copy_at(Stage<1>{}, Stage<I>{});
+                    __builtin_amdgcn_sched_barrier(0);
+                });
+            }
+            // ---- dV/dK of block 0 with the softmax of block 1 ----
+            f32x4_t l41[4], d41[4];
+            block_rows(sb, 1, l41, d41);
+            block_mask(s1, q0 + 32);
+            float pr1[16], dr1[16];
+            u32x4_t pp1[2], dsp1[2];
+            auto pv_stream = [&](const char* qblk, u32x4_t (&pp)[2], u32x4_t (&dsp)[2], auto with_soft) {
+                u32x4_t ring[KA];
+                // instruction i: chunk kc = i / 8, d tile dt = (i / 2) % 4,
+                // even -> dV (dO^T operand), odd -> dK (Q^T operand)
+                auto fetch = [&](auto f_tag) {
+                    constexpr int F = decltype(f_tag)::value, kc = F / 8, dt = (F / 2) % NDT;
+                    const char* base = qblk + kc * 16 * RB + (F % 2 ? 0 : TQ);
+                    ring[F % KA] = tr_pair(base + rt[0][dt], base + rt[1][dt]);
+                };
+                static_for<KA>([&](auto f) { fetch(f); });
+                static_for<4 * NDT>([&](auto i_tag) {
+                    constexpr int I = decltype(i_tag)::value, kc = I / 8, dt = (I / 2) % NDT;
+                    const u32x4_t a = ring[I % KA];
+                    if constexpr (I + KA < 4 * NDT) fetch(Stage<I + KA>{});
+                    if constexpr (I % 2 == 0) dva[dt] = mfma16(a, pp[kc], dva[dt], BF16);
+                    else dka[dt] = mfma16(a, dsp[kc], dka[dt], BF16);
+                    with_soft(Stage<I>{});
+                    __builtin_amdgcn_sched_barrier(0);
+                });
+            };
+            pv_stream(sb, pp0, dsp0, [&](auto i_tag) {
+                constexpr int I = decltype(i_tag)::value;
+                if constexpr (I < 16) {
+                    soft_el(I, s1, dp1, l41, d41, pr1, dr1, pp1, dsp1);
+                    asm volatile("" : "+v"(pr1[I]), "+v"(dr1[I]));
                 }
-            }
-
-            // ---- P = exp2(c s - LSE log2 e), dS = P (dP - D); accumulator row
-            //      r holds query 8(r/4) + 4g + r%4 of the block ----
-            f32x4_t l4[4], d4[4];
-#pragma unroll
-            for (int rb = 0; rb < 4; ++rb) {
-                l4[rb] = *(const f32x4_t*)(sb + OFF_LSE + (32 * qb + 8 * rb + 4 * g) * 4);
-                d4[rb] = *(const f32x4_t*)(sb + OFF_D + (32 * qb + 8 * rb + 4 * g) * 4);
-            }
-            // masks (diagonal and ragged blocks only, a wave-uniform branch
-            // around one pass): score rr belongs to query qbase + 4g + off(rr)
-            // and lives iff key <= query < sq; dead scores become -inf * sign(c)
-            // (c is never zero), so their probability and dS are exactly 0.
-            // The select is a sign mask and a bit-field insert, one pass before
-            // the exponentials.
-            const bool need_mask = (qbase + 32 > sq) || (CAUSAL && qbase < n0 + 32 * w + 31);
-            if (need_mask) {
-                const int lo = CAUSAL ? key - qbase - 4 * g : -(1 << 20);
-                const int hi1 = sq - qbase - 4 * g - 1;
-#pragma unroll
-                for (int rr = 0; rr < 16; ++rr) {
-                    const int off = (rr >> 2) * 8 + (rr & 3);
-                    const uint32_t dead = (uint32_t)(((off - lo) | (hi1 - off)) >> 31);
-                    const float x = s[rr];  // through a scalar: a bit cast of a vector element reads element 0
-                    const uint32_t bits = __builtin_bit_cast(uint32_t, x);
-                    s[rr] = __builtin_bit_cast(float, (bits & ~dead) | (dead_bits & dead));
-                }
-            }
-            u32x4_t pp[2], dsp[2];
-#pragma unroll
-            for (int r = 0; r < 16; r += 2) {
-                float pr[2], dr[2];
-#pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    const int rr = r + e;
-                    const float pv = fast_exp2(__builtin_fmaf(s[rr], c, -l4[rr >> 2][rr & 3]));
-                    pr[e] = pv;
-                    dr[e] = pv * (dp[rr] - d4[rr >> 2][rr & 3]);
-                }
-                pp[r >> 3][(r >> 1) & 3] = pack2(pr[0], pr[1], BF16);
-                dsp[r >> 3][(r >> 1) & 3] = pack2(dr[0], dr[1], BF16);
-            }
-
-            // ---- dV^T += dO^T P and dK^T += Q^T dS over this block's queries ----
-#pragma unroll
-            for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-                for (int dt = 0; dt < NDT; ++dt) {
-                    dva[dt] = mfma16(opg[kc][dt], pp[kc], dva[dt], BF16);
-                    dka[dt] = mfma16(opq[kc][dt], dsp[kc], dka[dt], BF16);
-                }
+                copy_at(Stage<2>{}, i_tag);
+            });
+            // ---- dV/dK of block 1 ----
+            pv_stream(sb + 32 * RB, pp1, dsp1, [&](auto) {});
+        } else {
+            static_for<2 * DMA>([&](auto c) { copy_one(Stage<S ^ 1>{}, c, qn); });
+            if (ok0) compute_block(sb, 0, q0);
+            if (ok1) compute_block(sb, 1, q0 + 32);
         }
     };
 
@@ -321,11 +456,9 @@ fa_bwd_dkdv(BwdParams p)
         store_rows(S);
         wait_copies();
         __syncthreads();  // stage S is complete; every wave is done with stage S^1
-        if (t + 1 < qs_end) {
-            issue(Stage<S ^ 1>{}, (t + 1) * BMQ);
-            fetch_rows((t + 1) * BMQ);
-        }
-        compute(st_tag, t * BMQ);
+        const int qn = (t + 1 < qs_end ? t + 1 : t) * BMQ;
+        fetch_rows(qn);
+        compute(st_tag, t * BMQ, qn);
     };
 
     if (qs_begin < qs_end) {
