@@ -25,6 +25,7 @@ raise.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import math
 import os
@@ -51,52 +52,92 @@ class FaError(RuntimeError):
         self.code = code
 
 
+def _declare(L):
+    """Argument and result types of every exported entry point."""
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    L.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                         ctypes.c_float, ctypes.c_int, ctypes.c_int, vp]
+    L.fa_fwd.restype = ctypes.c_int
+    ip = ctypes.POINTER(ctypes.c_int)
+    L.fa_query_config.argtypes = [ctypes.c_int, i64, ctypes.c_int, i64, i64, i64, i64, ip, ip, ip, ip]
+    L.fa_query_config.restype = ctypes.c_int
+    L.fa_query_launch.argtypes = [ctypes.c_int, i64, ctypes.c_int, i64, i64, i64, i64, ip, ip]
+    L.fa_query_launch.restype = ctypes.c_int
+    L.fa_last_error.argtypes = []
+    L.fa_last_error.restype = ctypes.c_char_p
+    L.fa_version.argtypes = []
+    L.fa_version.restype = ctypes.c_int
+    L.fa_fwd_split.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                               ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                               vp, ctypes.c_size_t, vp]
+    L.fa_fwd_split.restype = ctypes.c_int
+    L.fa_fwd_split_noalloc.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                                       ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
+    L.fa_fwd_split_noalloc.restype = ctypes.c_int
+    L.fa_split_workspace_bytes.argtypes = [i64, i64, i64, i64, ctypes.c_int]
+    L.fa_split_workspace_bytes.restype = ctypes.c_size_t
+    L.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
+                                ctypes.c_float, ctypes.c_int, ctypes.c_int, vp]
+    L.fa_fwd_varlen.restype = ctypes.c_int
+    L.fa_bwd.argtypes = [vp] * 10 + [ctypes.c_size_t, i64, i64, i64, i64, i64,
+                                     ctypes.c_float, ctypes.c_int, ctypes.c_int, vp]
+    L.fa_bwd.restype = ctypes.c_int
+    L.fa_bwd_workspace_bytes.argtypes = [i64, i64, i64]
+    L.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
+    L.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float,
+                             ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_int, vp]
+    L.fa_fwd_fp8.restype = ctypes.c_int
+    L.fa_clock_probe.argtypes = [vp, i64, vp]
+    L.fa_clock_probe.restype = ctypes.c_int
+
+
 def lib() -> ctypes.CDLL:
     """Load libfa.so (raises if it has not been built)."""
     global _lib
     with _lock:
+        if _routed is not None:
+            return _routed
         if _lib is not None:
             return _lib
         if not os.path.exists(LIB_PATH):
             raise RuntimeError("libfa.so is not built; run python -m exact_attention_86_amd.build")
         L = ctypes.CDLL(LIB_PATH)
-        vp, i64 = ctypes.c_void_p, ctypes.c_int64
-        L.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
-                             ctypes.c_float, ctypes.c_int, ctypes.c_int, vp]
-        L.fa_fwd.restype = ctypes.c_int
-        ip = ctypes.POINTER(ctypes.c_int)
-        L.fa_query_config.argtypes = [ctypes.c_int, i64, ctypes.c_int, i64, i64, i64, i64, ip, ip, ip, ip]
-        L.fa_query_config.restype = ctypes.c_int
-        L.fa_query_launch.argtypes = [ctypes.c_int, i64, ctypes.c_int, i64, i64, i64, i64, ip, ip]
-        L.fa_query_launch.restype = ctypes.c_int
-        L.fa_last_error.argtypes = []
-        L.fa_last_error.restype = ctypes.c_char_p
-        L.fa_version.argtypes = []
-        L.fa_version.restype = ctypes.c_int
-        L.fa_fwd_split.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
-                                   ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                   vp, ctypes.c_size_t, vp]
-        L.fa_fwd_split.restype = ctypes.c_int
-        L.fa_fwd_split_noalloc.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
-                                           ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
-        L.fa_fwd_split_noalloc.restype = ctypes.c_int
-        L.fa_split_workspace_bytes.argtypes = [i64, i64, i64, i64, ctypes.c_int]
-        L.fa_split_workspace_bytes.restype = ctypes.c_size_t
-        L.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
-                                    ctypes.c_float, ctypes.c_int, ctypes.c_int, vp]
-        L.fa_fwd_varlen.restype = ctypes.c_int
-        L.fa_bwd.argtypes = [vp] * 10 + [ctypes.c_size_t, i64, i64, i64, i64, i64,
-                                         ctypes.c_float, ctypes.c_int, ctypes.c_int, vp]
-        L.fa_bwd.restype = ctypes.c_int
-        L.fa_bwd_workspace_bytes.argtypes = [i64, i64, i64]
-        L.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
-        L.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float,
-                                 ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_int, vp]
-        L.fa_fwd_fp8.restype = ctypes.c_int
-        L.fa_clock_probe.argtypes = [vp, i64, vp]
-        L.fa_clock_probe.restype = ctypes.c_int
+        _declare(L)
         _lib = L
         return L
+
+
+POISON_LIB_PATH = os.path.join(PKG, "libfa_poison.so")
+_poison_lib = None
+_routed = None
+
+
+def poison_lib():
+    """Load the debug build libfa_poison.so: the same entry points, with every
+    global->LDS copy preceded by a NaN fill of its destination.  For race
+    tests only; raises if it has not been built."""
+    global _poison_lib
+    with _lock:
+        if _poison_lib is None:
+            if not os.path.exists(POISON_LIB_PATH):
+                raise RuntimeError("libfa_poison.so is not built; run python -m exact_attention_86_amd.build")
+            L = ctypes.CDLL(POISON_LIB_PATH)
+            _declare(L)
+            _poison_lib = L
+        return _poison_lib
+
+
+@contextlib.contextmanager
+def poisoned():
+    """Route every call of this module to the debug build libfa_poison.so
+    while the block runs (race tests; not thread-safe)."""
+    global _routed
+    L = poison_lib()
+    _routed = L
+    try:
+        yield L
+    finally:
+        _routed = None
 
 
 def fa_last_error() -> str:

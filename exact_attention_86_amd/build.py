@@ -15,7 +15,12 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfa.so")
+# debug build of the same library: every global->LDS copy first fills its
+# destination with NaN (FA_LDS_POISON), so a read of a stage before its copy
+# has landed surfaces in the outputs; used by the race tests only
+POISON_LIB = os.path.join(PKG, "libfa_poison.so")
 SOURCES = ["fa_api.cpp", "fa_fwd_kernels.hip", "fa_bwd_kernels.hip", "fa_fp8_kernels.hip", "fa_probe.hip"]
+POISONED = ["fa_fwd_kernels.hip", "fa_bwd_kernels.hip", "fa_fp8_kernels.hip"]  # the sources with copies
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -27,18 +32,22 @@ def hip_flags():
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every source (in parallel) and link libfa.so; returns its path."""
-    objs, procs = [], []
-    for src in SOURCES:
+    """Compile every source (in parallel) and link libfa.so and the debug
+    libfa_poison.so; returns the path of libfa.so."""
+    objs, pobjs, procs = [], [], []
+    jobs = [(src, "", False) for src in SOURCES] + [(src, ".poison", True) for src in POISONED]
+    for src, tag, poison in jobs:
         path = os.path.join(CSRC, src)
-        obj = os.path.join(CSRC, src + ".o")
+        obj = os.path.join(CSRC, src + tag + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        cmd = [HIPCC] + hip_flags() + lang + ["-c", path, "-o", obj]
+        cmd = [HIPCC] + hip_flags() + (["-DFA_LDS_POISON"] if poison else []) + lang + ["-c", path, "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
-        procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE,
-                                            stderr=subprocess.PIPE, text=True)))
+        procs.append((src + tag, subprocess.Popen(cmd, stdout=subprocess.PIPE,
+                                                  stderr=subprocess.PIPE, text=True)))
         objs.append(obj)
+        if poison:
+            pobjs.append(obj)
     failed = []
     for src, p in procs:
         _, err = p.communicate()
@@ -49,12 +58,15 @@ def build(verbose: bool = False) -> str:
             print("\n".join(errs), file=sys.stderr)
     if failed:
         raise RuntimeError("\n".join(failed))
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC"] + objs + ["-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    plain = [o for o in objs if ".poison." not in o]
+    debug = [os.path.join(CSRC, s + ".o") for s in SOURCES if s not in POISONED] + pobjs
+    for lib, members in ((LIB, plain), (POISON_LIB, debug)):
+        tmp = lib + ".tmp%d" % os.getpid()
+        cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC"] + members + ["-o", tmp]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, lib)
     for obj in objs:
         os.remove(obj)
     return LIB

@@ -52,19 +52,6 @@ __device__ __forceinline__ uint32_t lds_addr(const void* ptr)
     return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) char*)ptr);
 }
 
-// One 1 KiB global -> LDS copy: lane i's 16 bytes at sbase + voff land at LDS
-// byte address lds_base + 16 i.  Issued as inline assembly so the compiler does
-// not serialise the other stage's LDS reads behind it; completion is awaited
-// explicitly with wait_copies() before the barrier that publishes the stage.
-template <int IMM>
-__device__ __forceinline__ void copy_1k(const void* sbase, uint32_t voff, uint32_t lds_base)
-{
-    asm volatile("s_add_u32 m0, %0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-                 :
-                 : "s"(lds_base), "v"(voff), "s"(sbase), "n"(IMM)
-                 : "memory", "m0", "scc");
-}
-
 // a pointer the compiler cannot prove wave-uniform, moved to scalar registers
 // (the caller knows it is uniform)
 __device__ __forceinline__ const void* uniform_ptr(const void* ptr)
@@ -73,6 +60,33 @@ __device__ __forceinline__ const void* uniform_ptr(const void* ptr)
     const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
     const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
     return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
+// One 1 KiB global -> LDS copy: lane i's 16 bytes at sbase + voff land at LDS
+// byte address lds_base + 16 i.  Issued as inline assembly so the compiler does
+// not serialise the other stage's LDS reads behind it; completion is awaited
+// explicitly with wait_copies() before the barrier that publishes the stage.
+template <int IMM>
+__device__ __forceinline__ void copy_1k(const void* sbase, uint32_t voff, uint32_t lds_base)
+{
+#ifdef FA_LDS_POISON
+    // Debug build (libfa_poison.so): this lane's 16 destination bytes are set
+    // to all ones (NaN in fp16, bf16 and E4M3) just before the copy is issued.
+    // A wave that reads a stage before its copies have landed, or a copy into
+    // a stage another wave still reads, then shows up as NaN in the outputs
+    // instead of as stale finite data.
+    // (the base address and source pointer are wave-uniform: the callers say
+    // so, and the copy below needs them in scalar registers)
+    lds_base = __builtin_amdgcn_readfirstlane(lds_base);
+    sbase = uniform_ptr(sbase);
+    typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
+    *(lds_u32x4_t*)(uintptr_t)(lds_base + IMM + 16u * (threadIdx.x & 63u)) = u32x4_t{~0u, ~0u, ~0u, ~0u};
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#endif
+    asm volatile("s_add_u32 m0, %0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :
+                 : "s"(lds_base), "v"(voff), "s"(sbase), "n"(IMM)
+                 : "memory", "m0", "scc");
 }
 
 __device__ __forceinline__ void wait_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }

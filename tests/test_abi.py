@@ -448,3 +448,15 @@ def test_clock_probe_argument_checks():
     assert L_.fa_clock_probe(A, 0, None) == fa.FA_ERR_INVALID_ARG
     assert L_.fa_clock_probe(A, 10000001, None) == fa.FA_ERR_INVALID_ARG
     assert L_.fa_clock_probe(A + 4, 2000, None) == fa.FA_ERR_MISALIGNED
+
+
+def test_poison_debug_build_exports_every_declared_symbol():
+    # the debug build of the race tests is the same library with its copies
+    # preceded by NaN fills; it must offer the same entry points
+    L_ = fa.poison_lib()
+    for name in declared_symbols():
+        assert hasattr(L_, name), name
+    assert L_.fa_version() == fa.fa_version()
+    with fa.poisoned() as routed:
+        assert fa.lib() is routed
+    assert fa.lib() is not L_
