@@ -419,7 +419,7 @@ FA_API int fa_bwd(const void* q, const void* k, const void* v, const void* o, co
     if (!isfinite(scale)) return fail(FA_ERR_INVALID_ARG, "fa_bwd: scale must be finite");
     if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARG, "fa_bwd: causal must be 0 or 1");
     if (d > 4096 || !fa::bwd_supported(dtype, (int)d))
-        return fail(FA_ERR_UNSUPPORTED, "fa_bwd: fp16/bf16 with d = 128 only");
+        return fail(FA_ERR_UNSUPPORTED, "fa_bwd: fp16/bf16 with d = 64 or 128 only");
     if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)dout | (uintptr_t)dq |
          (uintptr_t)dk | (uintptr_t)dv | (uintptr_t)workspace) & 15u)
         return fail(FA_ERR_MISALIGNED, "fa_bwd: tensors and workspace must be 16-byte aligned");

@@ -44,13 +44,20 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-// 16-byte chunk swizzle for 256-byte rows that are read both as 16-byte row
-// fragments (16 consecutive rows at one logical chunk: the map is a bijection
-// on the low four row bits, so they cover the 16 chunk positions of a bank
-// line) and with 8-byte transpose reads (4 consecutive rows x 4 consecutive
-// chunks: row bits 0-1 move chunk bits 2-3, so the 4 rows fall in different
-// 4-chunk groups).
-__device__ __forceinline__ int swz_b(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+// 16-byte chunk swizzle for rows of CPR chunks that are read both as 16-byte
+// row fragments (16 consecutive rows at one logical chunk) and with 8-byte
+// transpose reads (4 consecutive rows x 4 consecutive chunks).  256-byte rows
+// (CPR = 16): a bijection on the low four row bits, so 16 rows cover the 16
+// chunk positions of a 256-byte bank line, and row bits 0-1 move chunk bits
+// 2-3, so the 4 rows of a transpose read fall in different 4-chunk groups.
+// 128-byte rows (CPR = 8): the row's parity already picks the half of a bank
+// line, and row bits 1-3 pick the chunk, so 16 rows cover all 16 positions.
+template <int CPR>
+__device__ __forceinline__ int swz_b(int row)
+{
+    if constexpr (CPR == 16) return ((row & 3) << 2) | ((row >> 2) & 3);
+    return (row >> 1) & 7;
+}
 
 __device__ __forceinline__ float widen16(uint32_t bits, bool bf16)
 {
@@ -106,7 +113,8 @@ template <int D, bool BF16, bool CAUSAL>
 __global__ void __launch_bounds__(256, 1)
 fa_bwd_dkdv(BwdParams p)
 {
-    static_assert(D == 128, "256-byte rows");
+    static_assert(D == 64 || D == 128, "128- or 256-byte rows");
+    constexpr int CPR = D / 8;            // 16-byte chunks per row
     constexpr int NW = 4;                 // waves; wave w owns keys [32w, 32w+32)
     constexpr int BN = 32 * NW;           // keys per workgroup
     constexpr int BMQ = 64;               // queries per step (two 32-row blocks)
@@ -165,15 +173,15 @@ fa_bwd_dkdv(BwdParams p)
 #pragma unroll
     for (int j = 0; j < DMA; ++j) {
         const int cc = (w * DMA + j) * 64 + lane;
-        const int row = cc >> 4, pch = cc & 15;
-        cof[j] = row * RB + ((pch ^ swz_b(row)) << 4);
+        const int row = cc / CPR, pch = cc % CPR;
+        cof[j] = row * RB + ((pch ^ swz_b<CPR>(row)) << 4);
     }
     // copy C (0..2*DMA-1: Q copies, then dO copies) of the tile at query q0
     // into stage ST; rows past the last query re-read it (masked later), by
     // arithmetic, so a copy is one branch-free instruction
     auto copy_one = [&](auto st_tag, auto c_tag, int q0) {
         constexpr int ST = decltype(st_tag)::value, C = decltype(c_tag)::value, J = C % DMA;
-        const int row = ((w * DMA + J) * 64 + lane) >> 4;
+        const int row = ((w * DMA + J) * 64 + lane) / CPR;
         const uint32_t off = cof[J] - (uint32_t)(max(row - (sq - 1 - q0), 0) * RB);
         const void* src = uniform_ptr((C < DMA ? Q : dO) + (size_t)q0 * D);
         copy_1k<ST * STAGE + (C < DMA ? 0 : TQ) + J * 1024>(src, off, lbase);
@@ -188,8 +196,8 @@ fa_bwd_dkdv(BwdParams p)
             uint32_t off = cof[J];
             if (!full) {  // rows past the last query re-read it (masked later)
                 const int cc = (w * DMA + J) * 64 + lane;
-                const int row = cc >> 4, pch = cc & 15;
-                off = min(row, sq - 1 - q0) * RB + ((pch ^ swz_b(row)) << 4);
+                const int row = cc / CPR, pch = cc % CPR;
+                off = min(row, sq - 1 - q0) * RB + ((pch ^ swz_b<CPR>(row)) << 4);
             }
             copy_1k<ST * STAGE + J * 1024>(qsrc, off, lbase);
             copy_1k<ST * STAGE + TQ + J * 1024>(gsrc, off, lbase);
@@ -213,7 +221,7 @@ fa_bwd_dkdv(BwdParams p)
     //  row fragments (A operand of S and dP): row l32, logical chunk 2kk + g
     uint32_t rq[NKK];
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) rq[kk] = l32 * RB + (((2 * kk + g) ^ swz_b(l32)) << 4);
+    for (int kk = 0; kk < NKK; ++kk) rq[kk] = l32 * RB + (((2 * kk + g) ^ swz_b<CPR>(l32)) << 4);
     //  transpose reads (A operand of dV^T and dK^T): lane 4r + c of its 16-lane
     //  group reads query row 8j + 4g + r, d = 32dt + 16*half + 4c
     const int sub = lane & 15, tr_r = sub >> 2, tr_c = sub & 3, half = (lane >> 4) & 1;
@@ -223,7 +231,7 @@ fa_bwd_dkdv(BwdParams p)
         const int row = 8 * j + 4 * g + tr_r;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
-            rt[j][dt] = row * RB + (((4 * dt + 2 * half + (tr_c >> 1)) ^ swz_b(row)) << 4) + (tr_c & 1) * 8;
+            rt[j][dt] = row * RB + (((4 * dt + 2 * half + (tr_c >> 1)) ^ swz_b<CPR>(row)) << 4) + (tr_c & 1) * 8;
     }
 
     f32x16_t dva[NDT], dka[NDT];
@@ -348,7 +356,7 @@ fa_bwd_dkdv(BwdParams p)
                                      : (I == 2 ? 5 : I == 7 ? 6 : I == 12 ? 7 : -1);
             if constexpr (C >= 0 && C < 2 * DMA) copy_one(Stage<S ^ 1>{}, Stage<C>{}, qn);
         };
-        static_assert(2 * DMA == 8, "eight copies per wave per step");
+        static_assert(2 * DMA <= 8, "copy slots for at most eight copies per wave per step");
         if (ok0 && ok1) {
             constexpr int KA = 4;
             // ---- S/dP of block 0 ----
@@ -402,8 +410,13 @@ fa_bwd_dkdv(BwdParams p)
                     if constexpr (I + KA < 2 * NKK) fetch(Stage<I + KA>{});
                     if constexpr (I % 2 == 0) s1 = mfma16(a, kf[I / 2], s1, BF16);
                     else dp1 = mfma16(a, vf[I / 2], dp1, BF16);
-                    soft_el(I, s0, dp0, l40, d40, pr0, dr0, pp0, dsp0);
-                    asm volatile("" : "+v"(pr0[I]), "+v"(dr0[I]));
+                    // the block's 16 softmax elements spread evenly over the stream
+                    constexpr int EPS = 16 / (2 * NKK);
+                    static_for<EPS>([&](auto j_tag) {
+                        constexpr int E = I * EPS + decltype(j_tag)::value;
+                        soft_el(E, s0, dp0, l40, d40, pr0, dr0, pp0, dsp0);
+                        asm volatile("" : "+v"(pr0[E]), "+v"(dr0[E]));
+                    });
                     copy_at(Stage<1>{}, Stage<I>{});
                     __builtin_amdgcn_sched_barrier(0);
                 });
@@ -416,16 +429,16 @@ fa_bwd_dkdv(BwdParams p)
             u32x4_t pp1[2], dsp1[2];
             auto pv_stream = [&](const char* qblk, u32x4_t (&pp)[2], u32x4_t (&dsp)[2], auto with_soft) {
                 u32x4_t ring[KA];
-                // instruction i: chunk kc = i / 8, d tile dt = (i / 2) % 4,
+                // instruction i: chunk kc = i / (2 NDT), d tile dt = (i / 2) % NDT,
                 // even -> dV (dO^T operand), odd -> dK (Q^T operand)
                 auto fetch = [&](auto f_tag) {
-                    constexpr int F = decltype(f_tag)::value, kc = F / 8, dt = (F / 2) % NDT;
+                    constexpr int F = decltype(f_tag)::value, kc = F / (2 * NDT), dt = (F / 2) % NDT;
                     const char* base = qblk + kc * 16 * RB + (F % 2 ? 0 : TQ);
                     ring[F % KA] = tr_pair(base + rt[0][dt], base + rt[1][dt]);
                 };
                 static_for<KA>([&](auto f) { fetch(f); });
                 static_for<4 * NDT>([&](auto i_tag) {
-                    constexpr int I = decltype(i_tag)::value, kc = I / 8, dt = (I / 2) % NDT;
+                    constexpr int I = decltype(i_tag)::value, kc = I / (2 * NDT), dt = (I / 2) % NDT;
                     const u32x4_t a = ring[I % KA];
                     if constexpr (I + KA < 4 * NDT) fetch(Stage<I + KA>{});
                     if constexpr (I % 2 == 0) dva[dt] = mfma16(a, pp[kc], dva[dt], BF16);
@@ -436,10 +449,12 @@ fa_bwd_dkdv(BwdParams p)
             };
             pv_stream(sb, pp0, dsp0, [&](auto i_tag) {
                 constexpr int I = decltype(i_tag)::value;
-                if constexpr (I < 16) {
-                    soft_el(I, s1, dp1, l41, d41, pr1, dr1, pp1, dsp1);
-                    asm volatile("" : "+v"(pr1[I]), "+v"(dr1[I]));
-                }
+                constexpr int EPS = 16 / (4 * NDT);
+                static_for<EPS>([&](auto j_tag) {
+                    constexpr int E = I * EPS + decltype(j_tag)::value;
+                    soft_el(E, s1, dp1, l41, d41, pr1, dr1, pp1, dsp1);
+                    asm volatile("" : "+v"(pr1[E]), "+v"(dr1[E]));
+                });
                 copy_at(Stage<2>{}, i_tag);
             });
             // ---- dV/dK of block 1 ----
@@ -498,7 +513,8 @@ template <int D, bool BF16, bool CAUSAL>
 __global__ void __launch_bounds__(256, 2)
 fa_bwd_dq(BwdParams p)
 {
-    static_assert(D == 128, "256-byte rows");
+    static_assert(D == 64 || D == 128, "128- or 256-byte rows");
+    constexpr int CPR = D / 8;            // 16-byte chunks per row
     constexpr int NW = 4;                 // waves; wave w owns queries [32w, 32w+32)
     constexpr int BM = 32 * NW;           // queries per workgroup
     constexpr int BN = 64;                // keys per step (two 32-key blocks)
@@ -553,8 +569,8 @@ fa_bwd_dq(BwdParams p)
 #pragma unroll
     for (int j = 0; j < DMA; ++j) {
         const int cc = (w * DMA + j) * 64 + lane;
-        const int row = cc >> 4, pch = cc & 15;
-        cof[j] = row * RB + ((pch ^ swz_b(row)) << 4);
+        const int row = cc / CPR, pch = cc % CPR;
+        cof[j] = row * RB + ((pch ^ swz_b<CPR>(row)) << 4);
     }
     auto issue = [&](auto st_tag, int n0) {
         constexpr int ST = decltype(st_tag)::value;
@@ -566,8 +582,8 @@ fa_bwd_dq(BwdParams p)
             uint32_t off = cof[J];
             if (!full) {  // rows past the last key re-read it (masked)
                 const int cc = (w * DMA + J) * 64 + lane;
-                const int row = cc >> 4, pch = cc & 15;
-                off = min(row, sk - 1 - n0) * RB + ((pch ^ swz_b(row)) << 4);
+                const int row = cc / CPR, pch = cc % CPR;
+                off = min(row, sk - 1 - n0) * RB + ((pch ^ swz_b<CPR>(row)) << 4);
             }
             copy_1k<ST * STAGE + J * 1024>(ksrc, off, lbase);
             copy_1k<ST * STAGE + TK + J * 1024>(vsrc, off, lbase);
@@ -576,7 +592,7 @@ fa_bwd_dq(BwdParams p)
 
     uint32_t rk[NKK];
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) rk[kk] = l32 * RB + (((2 * kk + g) ^ swz_b(l32)) << 4);
+    for (int kk = 0; kk < NKK; ++kk) rk[kk] = l32 * RB + (((2 * kk + g) ^ swz_b<CPR>(l32)) << 4);
     const int sub = lane & 15, tr_r = sub >> 2, tr_c = sub & 3, half = (lane >> 4) & 1;
     uint32_t rt[2][NDT];
 #pragma unroll
@@ -584,7 +600,7 @@ fa_bwd_dq(BwdParams p)
         const int row = 8 * j + 4 * g + tr_r;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
-            rt[j][dt] = row * RB + (((4 * dt + 2 * half + (tr_c >> 1)) ^ swz_b(row)) << 4) + (tr_c & 1) * 8;
+            rt[j][dt] = row * RB + (((4 * dt + 2 * half + (tr_c >> 1)) ^ swz_b<CPR>(row)) << 4) + (tr_c & 1) * 8;
     }
 
     f32x16_t dqa[NDT];
@@ -722,13 +738,17 @@ hipError_t launch_bwd_t(BwdParams p, hipStream_t s)
 
 }  // namespace
 
-bool bwd_supported(int dtype, int d) { return (dtype == 1 || dtype == 2) && d == 128; }
+bool bwd_supported(int dtype, int d) { return (dtype == 1 || dtype == 2) && (d == 64 || d == 128); }
 
 hipError_t launch_bwd(int dtype, int d, const BwdParams& p, hipStream_t stream)
 {
-    if (d != 128) return hipErrorInvalidValue;
-    if (dtype == 2) return launch_bwd_t<128, true>(p, stream);
-    if (dtype == 1) return launch_bwd_t<128, false>(p, stream);
+    if (d == 128) {
+        if (dtype == 2) return launch_bwd_t<128, true>(p, stream);
+        if (dtype == 1) return launch_bwd_t<128, false>(p, stream);
+    } else if (d == 64) {
+        if (dtype == 2) return launch_bwd_t<64, true>(p, stream);
+        if (dtype == 1) return launch_bwd_t<64, false>(p, stream);
+    }
     return hipErrorInvalidValue;
 }
 

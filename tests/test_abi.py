@@ -260,7 +260,7 @@ def call_bwd(**kw):
     (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARG),
     (dict(causal=2), fa.FA_ERR_INVALID_ARG),
     (dict(dtype=fa.FA_F32), fa.FA_ERR_UNSUPPORTED),
-    (dict(d=64), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=32), fa.FA_ERR_UNSUPPORTED),
     (dict(d=256), fa.FA_ERR_UNSUPPORTED),
     (dict(dtype=9), fa.FA_ERR_UNSUPPORTED),
     (dict(dq=DQ + 8), fa.FA_ERR_MISALIGNED),

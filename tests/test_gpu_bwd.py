@@ -77,15 +77,27 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("case", CASES, ids=lambda c: "%s_b%dh%d_sq%d_sk%d_%s_%s" % (
-    c[0], c[1], c[2], c[3], c[4], "causal" if c[5] else "full", c[6]))
+# the same backward kernels with d = 64 (128-byte rows, half the d tiles)
+CASES_D64 = [
+    ("bf16", 1, 2, 128, 128, True, None, 64),
+    ("f16", 2, 3, 200, 328, False, None, 64),
+    ("bf16", 1, 3, 333, 150, True, None, 64),
+    ("f16", 1, 2, 77, 1, True, None, 64),
+    ("bf16", 1, 2, 190, 140, False, -0.07, 64),
+    ("f16", 1, 2, 512, 512, True, 0.0, 64),
+]
+
+
+@pytest.mark.parametrize("case", CASES + CASES_D64, ids=lambda c: "%s_b%dh%d_sq%d_sk%d_%s_%s_d%d" % (
+    c[0], c[1], c[2], c[3], c[4], "causal" if c[5] else "full", c[6], c[7] if len(c) > 7 else 128))
 def test_bwd_matches_oracle(case):
-    dtype, b, h, sq, sk, causal, scale = case
-    w = W.shape("bwd", dtype, b, h, sq, sk, 128, causal, scale=scale, seed=17 * sq + sk)
+    dtype, b, h, sq, sk, causal, scale = case[:7]
+    d = case[7] if len(case) > 7 else 128
+    w = W.shape("bwd", dtype, b, h, sq, sk, d, causal, scale=scale, seed=17 * sq + sk + d)
     q, k, v = W.make(w)
     g = W.make_dout(w)
     s = float(np.float32(w.scale))
-    note(f"[bwd] {dtype} b{b} h{h} sq{sq} sk{sk} causal={causal} scale={s}")
+    note(f"[bwd] {dtype} b{b} h{h} sq{sq} sk{sk} d{d} causal={causal} scale={s}")
     dq, dk, dv = gpu_bwd(q, k, v, g, causal, s)
     rq, rk, rv = oracle.attn_bwd(q, k, v, g, s, causal)
     check("dq", dq, rq, dtype)
