@@ -671,7 +671,15 @@ fa_fwd_16pp(Params p)
 #pragma unroll
     for (int e = 0; e < NDT; ++e) rv[e] = VRead<CPR>::offset(e, v_row, vhalf, vc);
 
-    auto process = [&](const int mt) {
+    // process(DESC, mt): query tile mt, key tiles in ascending (DESC false) or
+    // descending order; window t works on key tile kt(t) = t or nkv-1-t.  A
+    // wave whose rows end early skips the key tiles past its own last one:
+    // the last windows (ascending) or the first ones (descending).  In either
+    // order the first tile a wave computes holds a live key for every one of
+    // its rows (the key at the tile's start is at most its first row), so no
+    // row starts from a fully masked tile.
+    auto process = [&](auto desc_tag, const int mt) {
+        constexpr bool DESC = decltype(desc_tag)::value;
         const int q0 = mt * BM;
         const int q_end = min(q0 + BM, sq);
         const int kv_end = CAUSAL ? min(q_end, sk) : sk;
@@ -681,11 +689,15 @@ fa_fwd_16pp(Params p)
         const int w_kv_end = (wq_end <= wq_first) ? 0 : (CAUSAL ? min(wq_end, sk) : sk);
         const int w_nkv = (w_kv_end + BN - 1) / BN;
         const int qrow = wq_first + l32;
+        const int t_first = DESC ? nkv - w_nkv : 0;  // this wave's windows [t_first, t_end)
+        const int t_end = DESC ? nkv : w_nkv;
+        auto key0 = [&](int t) { return (DESC ? nkv - 1 - t : t) * BN; };
 
-        // K(0) goes out before the Q loads
+        // K(kt(0)) goes out before the Q loads
         {
-            const bool f = BN <= sk;
-            static_for<DMA>([&](auto j) { copy_k(j, Stage<0>{}, 0, f); });
+            const int n0 = key0(0);
+            const bool f = n0 + BN <= sk;
+            static_for<DMA>([&](auto j) { copy_k(j, Stage<0>{}, n0, f); });
         }
         const uint16_t* qptr = Q + (size_t)min(qrow, sq - 1) * D + g * 8;
         u32x4_t qf[NKK];
@@ -834,27 +846,29 @@ fa_fwd_16pp(Params p)
             l_run += lsum;
         };
 
-        // copies of K(t+1) -> K stage (t+1)&1 and V(t) -> V stage t&1
+        // copies of K(kt(t+1)) -> K stage (t+1)&1 and V(kt(t)) -> V stage t&1
         auto issue = [&](auto kst_tag, auto vst_tag, int t) {
             if (t + 1 < nkv) {
-                const bool f = (t + 2) * BN <= sk;
-                static_for<DMA>([&](auto j) { copy_k(j, kst_tag, (t + 1) * BN, f); });
+                const int n0 = key0(t + 1);
+                const bool f = n0 + BN <= sk;
+                static_for<DMA>([&](auto j) { copy_k(j, kst_tag, n0, f); });
             }
             if (t < nkv) {
-                const bool f = (t + 1) * BN <= sk;
-                static_for<DMA>([&](auto j) { copy_v(j, vst_tag, t * BN, f); });
+                const int n0 = key0(t);
+                const bool f = n0 + BN <= sk;
+                static_for<DMA>([&](auto j) { copy_v(j, vst_tag, n0, f); });
             }
         };
 
-        // M(t) for this wave, t = tile index; TP = t & 1
+        // M(t) for this wave, t = window index; TP = t & 1
         auto do_m = [&](auto tp_tag, int t) {
             constexpr int TP = decltype(tp_tag)::value;
-            const bool ds = t < nkv && t < w_nkv;
-            const bool dp = t >= 1 && t - 1 < w_nkv;
+            const bool ds = t >= t_first && t < t_end;
+            const bool dp = t - 1 >= t_first && t - 1 < t_end;
             mphase(Stage<TP>{}, Stage<TP ^ 1>{}, ds, dp);
         };
         auto do_x = [&](int t) {
-            if (t >= 0 && t < w_nkv) xphase(t * BN);
+            if (t >= t_first && t < t_end) xphase(key0(t));
         };
 
         // prologue: K(0) resident for everyone
@@ -906,16 +920,23 @@ fa_fwd_16pp(Params p)
             if (!persist_unit(p, r, bh, mt)) break;
             set_head(bh);
             if (r > 0) __syncthreads();  // every wave is done with the LDS stages
-            process(mt);
+            process(Stage<0>{}, mt);
         }
     } else {
+        // the second tile of a causal pair walks its keys downwards.  The
+        // pairs of one head start together and cost the same, so pair i
+        // starts its second tile (i) after nQ - i query-tile times and ends
+        // with the others: walking down, every second tile of the head reads
+        // key block nQ - T at time T and they share it in L2, where walking
+        // up they would read block 0 again one after another, long after the
+        // first tiles read it
         set_head(bh);
         int mts[2];
         const int nt = item_tiles(p, item, mts);
-        process(mts[0]);
+        process(Stage<0>{}, mts[0]);
         if (nt > 1) {
             __syncthreads();  // every wave is done with the LDS stages
-            process(mts[1]);
+            process(Stage<1>{}, mts[1]);
         }
     }
 }

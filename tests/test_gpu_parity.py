@@ -279,11 +279,16 @@ def test_eight_waves_equal_four_waves(dt, h, sq, sk, causal, gpu):
     """The same problem through the 8-wave ping-pong kernel (fa_fwd on many
     heads) and through the 4-wave kernel (fa_fwd_varlen with one sequence per
     head set) gives the same bits: both run each 32-row query block through
-    the same instruction sequence per 64-key tile, so any difference means a
-    stage was read before its copy landed or after it was overwritten."""
+    the same instruction sequence per 64-key tile, in ascending key order, so
+    any difference means a stage was read before its copy landed or after it
+    was overwritten.  On the per-item causal grid the ping-pong kernel walks
+    the light tile of each pair (query tiles below nQ/2, 256 rows each) in
+    descending key order: those rows are the same sums in another order and
+    are held to the oracle's tolerance instead."""
     import torch
     cfg = fa.fa_query_config(W.DTYPE_CODE[dt], 128, int(causal), 1, h, sq, sk)
     assert cfg["waves"] == 8
+    launch = fa.fa_query_launch(W.DTYPE_CODE[dt], 128, int(causal), 1, h, sq, sk)
     w = W.shape("waves", dt, 1, h, sq, sk, 128, causal, seed=sq + sk)
     q, k, v = (t.cuda() for t in W.make(w))
     s = scale32(w.scale)
@@ -292,7 +297,13 @@ def test_eight_waves_equal_four_waves(dt, h, sq, sk, causal, gpu):
     cu_k = torch.tensor([0, sk], dtype=torch.int32, device="cuda")
     o4, l4 = fa.attention_varlen(q[0], k[0], v[0], cu_q, cu_k, sq, causal=causal, scale=s)
     torch.cuda.synchronize()
-    assert torch.equal(o8[0], o4) and torch.equal(l8[0], l4)
+    n_mt = -(-sq // cfg["block_m"])
+    desc = min(sq, (n_mt // 2) * cfg["block_m"]) if causal and not launch["persistent"] else 0
+    assert torch.equal(o8[0][:, desc:], o4[:, desc:]) and torch.equal(l8[0][:, desc:], l4[:, desc:])
+    if desc:
+        do = float((o8[0][:, :desc].float() - o4[:, :desc].float()).abs().max())
+        dl = float((l8[0][:, :desc] - l4[:, :desc]).abs().max())
+        assert do <= TOL_O[dt] and dl <= TOL_LSE, (do, dl)
 
 
 def test_stream_argument(gpu):
