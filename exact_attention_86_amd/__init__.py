@@ -84,6 +84,9 @@ def _declare(L):
     L.fa_bwd.restype = ctypes.c_int
     L.fa_bwd_workspace_bytes.argtypes = [i64, i64, i64]
     L.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
+    L.fa_bwd_varlen.argtypes = [vp] * 10 + [ctypes.c_size_t, vp, vp, i64, i64, i64, i64, i64, i64, i64,
+                                            ctypes.c_float, ctypes.c_int, ctypes.c_int, vp]
+    L.fa_bwd_varlen.restype = ctypes.c_int
     L.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float,
                              ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_int, vp]
     L.fa_fwd_fp8.restype = ctypes.c_int
@@ -223,6 +226,17 @@ def fa_fwd_fp8(q, k, v, o, lse, b, h, sq, sk, d, scale, descale_q, descale_k, de
     """The FP8 forward C entry point: device addresses as ints, returns the status code."""
     return lib().fa_fwd_fp8(q, k, v, o, lse, int(b), int(h), int(sq), int(sk), int(d), float(scale),
                             float(descale_q), float(descale_k), float(descale_v), int(causal), stream)
+
+
+def fa_bwd_varlen(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, cu_seqlens_q,
+                  cu_seqlens_k, batch, h, total_q, total_k, max_sq, max_sk, d, scale, causal, dtype,
+                  stream) -> int:
+    """The variable-length backward C entry point: device addresses as ints,
+    returns the status code."""
+    return lib().fa_bwd_varlen(q, k, v, o, dout, lse, dq, dk, dv, workspace, int(workspace_bytes),
+                               cu_seqlens_q, cu_seqlens_k, int(batch), int(h), int(total_q),
+                               int(total_k), int(max_sq), int(max_sk), int(d), float(scale),
+                               int(causal), int(dtype), stream)
 
 
 def fa_bwd_workspace_bytes(b, h, sq) -> int:
@@ -388,6 +402,59 @@ def attention_bwd(q, k, v, out, lse, dout, causal: bool = False, scale: float | 
     rc = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
                 lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
                 nbytes, b, h, sq, sk, d, scale, int(bool(causal)), _dtype_code(q), s.cuda_stream)
+    if rc != FA_OK:
+        raise FaError(rc, fa_last_error())
+    return dq, dk, dv
+
+
+def attention_bwd_varlen(q, k, v, out, lse, dout, cu_seqlens_q, cu_seqlens_k, max_sq: int, max_sk: int,
+                         causal: bool = False, scale: float | None = None, dq=None, dk=None, dv=None,
+                         workspace=None, stream=None):
+    """dQ, dK, dV for packed sequences: q, out, dout [h, total_q, d], k/v
+    [h, total_k, d], lse [h, total_q] fp32 as attention_varlen() returned
+    them for the same offsets, causal and scale; cu_seqlens_* int32 device
+    tensors of batch + 1 offsets.  Returns (dQ, dK, dV) without
+    synchronising."""
+    import torch
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise FaError(FA_ERR_INVALID_ARG, "q, k, v must be 3-d [h, total, d]")
+    h, total_q, d = q.shape
+    total_k = k.shape[1]
+    if tuple(k.shape) != (h, total_k, d) or tuple(v.shape) != (h, total_k, d):
+        raise FaError(FA_ERR_INVALID_ARG, "k and v must be [h, total_k, d] matching q")
+    if tuple(out.shape) != tuple(q.shape) or tuple(dout.shape) != tuple(q.shape):
+        raise FaError(FA_ERR_INVALID_ARG, "out and dout must have q's shape")
+    if tuple(lse.shape) != (h, total_q) or lse.dtype != torch.float32:
+        raise FaError(FA_ERR_INVALID_ARG, "lse must be fp32 [h, total_q]")
+    if not (q.dtype == k.dtype == v.dtype == out.dtype == dout.dtype):
+        raise FaError(FA_ERR_INVALID_ARG, "q, k, v, out, dout must share a dtype")
+    for name, t, shp in (("dq", dq, (h, total_q, d)), ("dk", dk, (h, total_k, d)), ("dv", dv, (h, total_k, d))):
+        if t is not None:
+            _check_buffer(name, t, shp, q.dtype, q.device)
+    if workspace is not None:
+        _check_buffer("workspace", workspace, None, None, q.device)
+    for t in (q, k, v, out, lse, dout, cu_seqlens_q, cu_seqlens_k):
+        if not (t.is_cuda and t.is_contiguous()):
+            raise FaError(FA_ERR_INVALID_ARG, "all tensors must be contiguous device tensors")
+    if cu_seqlens_q.dtype != torch.int32 or cu_seqlens_k.dtype != torch.int32:
+        raise FaError(FA_ERR_INVALID_ARG, "cu_seqlens must be int32")
+    if cu_seqlens_q.numel() != cu_seqlens_k.numel() or cu_seqlens_q.numel() < 2:
+        raise FaError(FA_ERR_INVALID_ARG, "cu_seqlens_q and cu_seqlens_k need batch + 1 entries each")
+    batch = cu_seqlens_q.numel() - 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    need = fa_bwd_workspace_bytes(1, h, total_q)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    nbytes = workspace.numel() * workspace.element_size()
+    s = stream if stream is not None else torch.cuda.current_stream(q.device)
+    rc = fa_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
+                       lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
+                       nbytes, cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), batch, h, total_q,
+                       total_k, max_sq, max_sk, d, scale, int(bool(causal)), _dtype_code(q), s.cuda_stream)
     if rc != FA_OK:
         raise FaError(rc, fa_last_error())
     return dq, dk, dv

@@ -407,6 +407,35 @@ FA_API size_t fa_bwd_workspace_bytes(int64_t b, int64_t h, int64_t sq)
     return (size_t)(b * h * sq) * 4;
 }
 
+// the backward's outputs and workspace (dq, dk, dv, D: nq, nk, nk, nw bytes)
+// must be disjoint from its inputs (q, k, v, o, dout: nq, nk, nk, nq, nq
+// bytes; lse: nl bytes) and from each other; returns the failing rule or null
+static const char* bwd_overlap(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                               const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t nq,
+                               size_t nk, size_t nl, size_t nw)
+{
+    const void* in[6] = {q, k, v, o, dout, lse};
+    const size_t in_n[6] = {nq, nk, nk, nq, nq, nl};
+    const void* outs[4] = {dq, dk, dv, workspace};
+    const size_t out_n[4] = {nq, nk, nk, nw};
+    for (int i = 0; i < 4; ++i) {
+        for (int j = 0; j < 6; ++j)
+            if (overlap(outs[i], out_n[i], in[j], in_n[j])) return "dq, dk, dv and workspace must not overlap the inputs";
+        for (int j = i + 1; j < 4; ++j)
+            if (overlap(outs[i], out_n[i], outs[j], out_n[j]))
+                return "dq, dk, dv and workspace must not overlap each other";
+    }
+    return nullptr;
+}
+
+// scale * log2(e), signed; a zero scale uses 1e-30 as the forward does
+// (exp2(1e-30 s) is exactly 1 in fp32), so c is never zero and a masked
+// score of -inf * sign(c) always exponentiates to 0
+static float bwd_exp_factor(float scale)
+{
+    return scale != 0.f ? (float)((double)scale * 1.4426950408889634) : 1e-30f;
+}
+
 FA_API int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                   const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
                   int64_t b, int64_t h, int64_t sq, int64_t sk, int64_t d, float scale, int causal,
@@ -432,18 +461,9 @@ FA_API int fa_bwd(const void* q, const void* k, const void* v, const void* o, co
         return fail(FA_ERR_INVALID_ARG, "fa_bwd: workspace smaller than fa_bwd_workspace_bytes()");
     const size_t nq = (size_t)(b * h * sq * d) * 2, nk = (size_t)(b * h * sk * d) * 2;
     const size_t nl = (size_t)(b * h * sq) * 4;
-    // outputs and workspace: disjoint from every input and from each other
-    const void* in[6] = {q, k, v, o, dout, lse};
-    const size_t in_n[6] = {nq, nk, nk, nq, nq, nl};
-    const void* outs[4] = {dq, dk, dv, workspace};
-    const size_t out_n[4] = {nq, nk, nk, need};
-    for (int i = 0; i < 4; ++i) {
-        for (int j = 0; j < 6; ++j)
-            if (overlap(outs[i], out_n[i], in[j], in_n[j]))
-                return fail(FA_ERR_INVALID_ARG, "fa_bwd: dq, dk, dv and workspace must not overlap the inputs");
-        for (int j = i + 1; j < 4; ++j)
-            if (overlap(outs[i], out_n[i], outs[j], out_n[j]))
-                return fail(FA_ERR_INVALID_ARG, "fa_bwd: dq, dk, dv and workspace must not overlap each other");
+    if (const char* why = bwd_overlap(q, k, v, o, dout, lse, dq, dk, dv, workspace, nq, nk, nl, need)) {
+        snprintf(g_err, sizeof g_err, "fa_bwd: %s", why);
+        return FA_ERR_INVALID_ARG;
     }
     const int64_t items = b * h * ((std::max(sq, sk) + 127) / 128);
     if (items > lim - 8) return fail(FA_ERR_TOO_LARGE, "fa_bwd: too many tiles for one launch");
@@ -462,17 +482,91 @@ FA_API int fa_bwd(const void* q, const void* k, const void* v, const void* o, co
     p.bh = (int)(b * h);
     p.sq = (int)sq;
     p.sk = (int)sk;
-    // signed exponent factor; a zero scale uses 1e-30 as the forward does
-    // (exp2(1e-30 s) is exactly 1 in fp32), so c is never zero and a masked
-    // score of -inf * sign(c) always exponentiates to 0
-    p.c = scale != 0.f ? (float)((double)scale * 1.4426950408889634) : 1e-30f;
+    p.c = bwd_exp_factor(scale);
     p.scale = scale;
     p.causal = causal;
     p.items_per_head = 0;
     p.n_items = 0;
+    p.cu_q = nullptr;
+    p.cu_k = nullptr;
+    p.batch = 1;
+    p.total_q = 0;
+    p.total_k = 0;
     hipError_t e = fa::launch_bwd(dtype, (int)d, p, (hipStream_t)stream);
     if (e != hipSuccess) {
         snprintf(g_err, sizeof g_err, "fa_bwd: launch failed: %s", hipGetErrorString(e));
+        return FA_ERR_HIP;
+    }
+    g_err[0] = 0;
+    return FA_OK;
+}
+
+FA_API int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                         const float* lse, void* dq, void* dk, void* dv, void* workspace,
+                         size_t workspace_bytes, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                         int64_t batch, int64_t h, int64_t total_q, int64_t total_k, int64_t max_sq,
+                         int64_t max_sk, int64_t d, float scale, int causal, int dtype, void* stream)
+{
+    if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace || !cu_seqlens_q ||
+        !cu_seqlens_k)
+        return fail(FA_ERR_INVALID_ARG, "fa_bwd_varlen: NULL pointer");
+    if (batch <= 0 || h <= 0 || total_q <= 0 || total_k <= 0 || max_sq <= 0 || max_sk <= 0 || d <= 0)
+        return fail(FA_ERR_INVALID_ARG,
+                    "fa_bwd_varlen: batch, h, total_q, total_k, max_sq, max_sk and d must be >= 1");
+    if (max_sq > total_q || max_sk > total_k)
+        return fail(FA_ERR_INVALID_ARG, "fa_bwd_varlen: max_sq / max_sk exceed total_q / total_k");
+    if (!isfinite(scale)) return fail(FA_ERR_INVALID_ARG, "fa_bwd_varlen: scale must be finite");
+    if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARG, "fa_bwd_varlen: causal must be 0 or 1");
+    if (d > 4096 || !fa::bwd_supported(dtype, (int)d))
+        return fail(FA_ERR_UNSUPPORTED, "fa_bwd_varlen: fp16/bf16 with d = 64 or 128 only");
+    if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)dout | (uintptr_t)dq |
+         (uintptr_t)dk | (uintptr_t)dv | (uintptr_t)workspace) & 15u)
+        return fail(FA_ERR_MISALIGNED, "fa_bwd_varlen: tensors and workspace must be 16-byte aligned");
+    if (((uintptr_t)lse | (uintptr_t)cu_seqlens_q | (uintptr_t)cu_seqlens_k) & 3u)
+        return fail(FA_ERR_MISALIGNED, "fa_bwd_varlen: lse and the offset arrays must be 4-byte aligned");
+    const int64_t lim = INT32_MAX;
+    if (total_q * d > lim || total_k * d > lim || h > lim || batch > lim - 1 || h * total_q > lim ||
+        h * batch > lim)
+        return fail(FA_ERR_TOO_LARGE, "fa_bwd_varlen: a per-head slice exceeds 2^31-1 elements");
+    const size_t need = fa_bwd_workspace_bytes(1, h, total_q);
+    if (workspace_bytes < need)
+        return fail(FA_ERR_INVALID_ARG, "fa_bwd_varlen: workspace smaller than fa_bwd_workspace_bytes(1, h, total_q)");
+    const size_t nq = (size_t)(h * total_q * d) * 2, nk = (size_t)(h * total_k * d) * 2;
+    const size_t nl = (size_t)(h * total_q) * 4;
+    if (const char* why = bwd_overlap(q, k, v, o, dout, lse, dq, dk, dv, workspace, nq, nk, nl, need)) {
+        snprintf(g_err, sizeof g_err, "fa_bwd_varlen: %s", why);
+        return FA_ERR_INVALID_ARG;
+    }
+    const int64_t items = h * batch * ((std::max(max_sq, max_sk) + 127) / 128);
+    if (items > lim - 8) return fail(FA_ERR_TOO_LARGE, "fa_bwd_varlen: too many tiles for one launch");
+
+    fa::BwdParams p;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.o = o;
+    p.dout = dout;
+    p.lse = lse;
+    p.dq = dq;
+    p.dk = dk;
+    p.dv = dv;
+    p.dvec = (float*)workspace;
+    p.bh = (int)(h * batch);  // (head, sequence) pairs
+    p.sq = (int)max_sq;       // grid sizes; each work item reads its own lengths
+    p.sk = (int)max_sk;
+    p.c = bwd_exp_factor(scale);
+    p.scale = scale;
+    p.causal = causal;
+    p.items_per_head = 0;
+    p.n_items = 0;
+    p.cu_q = cu_seqlens_q;
+    p.cu_k = cu_seqlens_k;
+    p.batch = (int)batch;
+    p.total_q = (int)total_q;
+    p.total_k = (int)total_k;
+    hipError_t e = fa::launch_bwd(dtype, (int)d, p, (hipStream_t)stream);
+    if (e != hipSuccess) {
+        snprintf(g_err, sizeof g_err, "fa_bwd_varlen: launch failed: %s", hipGetErrorString(e));
         return FA_ERR_HIP;
     }
     g_err[0] = 0;

@@ -75,6 +75,25 @@ __device__ __forceinline__ u32x4_t tr_pair(const char* a0, const char* a1)
                    __builtin_bit_cast(u32x2_t, x1)[0], __builtin_bit_cast(u32x2_t, x1)[1]};
 }
 
+// The rows one work item's (head, sequence) slice covers: its query and key
+// counts and the offsets of its first query and key row in the [.][D] arrays
+// (and of its first LSE / D entry).  Dense problems: slice bh of [bh][sq] and
+// [bh][sk].  Variable-length batches: bh = head * batch + sequence, the
+// sequence's rows taken from the offset arrays, clamped into [0, total] as the
+// forward does, so malformed offsets cannot address outside the buffers.
+struct Slice {
+    int sq, sk;
+    size_t q0, k0;
+};
+__device__ __forceinline__ Slice bwd_slice(const BwdParams& p, int bh)
+{
+    if (!p.cu_q) return Slice{p.sq, p.sk, (size_t)bh * p.sq, (size_t)bh * p.sk};
+    const int hd = bh / p.batch, s = bh - hd * p.batch;
+    const int qa = min(max(p.cu_q[s], 0), p.total_q), qb = min(max(p.cu_q[s + 1], qa), p.total_q);
+    const int ka = min(max(p.cu_k[s], 0), p.total_k), kb = min(max(p.cu_k[s + 1], ka), p.total_k);
+    return Slice{qb - qa, kb - ka, (size_t)hd * p.total_q + qa, (size_t)hd * p.total_k + ka};
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -131,22 +150,24 @@ fa_bwd_dkdv(BwdParams p)
 
     int bh, kt;
     if (!map_xcd_item(p.n_items, p.items_per_head, bh, kt)) return;
+    const Slice sl = bwd_slice(p, bh);
+    const int sq = sl.sq, sk = sl.sk;
+    const int n0 = kt * BN;
+    if (n0 >= sk) return;  // variable-length batch: past this sequence's keys
     const int tid = threadIdx.x;
     const int w = tid >> 6;
     const int lane = tid & 63;
     const int l32 = lane & 31;
     const int g = lane >> 5;
-    const int sq = p.sq, sk = p.sk;
-    const int n0 = kt * BN;
     const float c = p.c;
     const uint32_t dead_bits = c > 0.f ? 0xff800000u : 0x7f800000u;  // -inf * sign(c)
 
-    const uint16_t* __restrict__ Q = (const uint16_t*)p.q + (size_t)bh * sq * D;
-    const uint16_t* __restrict__ dO = (const uint16_t*)p.dout + (size_t)bh * sq * D;
-    const float* __restrict__ LSE = p.lse + (size_t)bh * sq;
-    const float* __restrict__ DV = p.dvec + (size_t)bh * sq;
-    const uint16_t* __restrict__ K = (const uint16_t*)p.k + (size_t)bh * sk * D;
-    const uint16_t* __restrict__ V = (const uint16_t*)p.v + (size_t)bh * sk * D;
+    const uint16_t* __restrict__ Q = (const uint16_t*)p.q + sl.q0 * D;
+    const uint16_t* __restrict__ dO = (const uint16_t*)p.dout + sl.q0 * D;
+    const float* __restrict__ LSE = p.lse + sl.q0;
+    const float* __restrict__ DV = p.dvec + sl.q0;
+    const uint16_t* __restrict__ K = (const uint16_t*)p.k + sl.k0 * D;
+    const uint16_t* __restrict__ V = (const uint16_t*)p.v + sl.k0 * D;
 
     // this wave's keys: B operands of S = Q K^T and dP = dO V^T (lane = key,
     // 8 d values per half-wave); keys past the end re-read the last key
@@ -490,8 +511,8 @@ fa_bwd_dkdv(BwdParams p)
     // ---- epilogue: dV = (dV^T)^T, dK = scale (dK^T)^T; accumulator row r of
     //      d tile dt is d = 32dt + 8(r/4) + 4g + r%4 ----
     if (key < sk) {
-        uint16_t* dvrow = (uint16_t*)p.dv + ((size_t)bh * sk + key) * D;
-        uint16_t* dkrow = (uint16_t*)p.dk + ((size_t)bh * sk + key) * D;
+        uint16_t* dvrow = (uint16_t*)p.dv + (sl.k0 + key) * D;
+        uint16_t* dkrow = (uint16_t*)p.dk + (sl.k0 + key) * D;
         const float sc = p.scale;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
@@ -529,21 +550,23 @@ fa_bwd_dq(BwdParams p)
 
     int bh, item;
     if (!map_xcd_item(p.n_items, p.items_per_head, bh, item)) return;
+    const Slice sl = bwd_slice(p, bh);
+    const int sq = sl.sq, sk = sl.sk;
+    const int mt = CAUSAL ? p.items_per_head - 1 - item : item;  // causal: heaviest tiles first
+    const int q0 = mt * BM;
+    if (q0 >= sq) return;  // variable-length batch: past this sequence's queries
     const int tid = threadIdx.x;
     const int w = tid >> 6;
     const int lane = tid & 63;
     const int l32 = lane & 31;
     const int g = lane >> 5;
-    const int sq = p.sq, sk = p.sk;
     const float c = p.c;
     const uint32_t dead_bits = c > 0.f ? 0xff800000u : 0x7f800000u;  // -inf * sign(c)
-    const int mt = CAUSAL ? p.items_per_head - 1 - item : item;  // causal: heaviest tiles first
-    const int q0 = mt * BM;
 
-    const uint16_t* __restrict__ Q = (const uint16_t*)p.q + (size_t)bh * sq * D;
-    const uint16_t* __restrict__ dO = (const uint16_t*)p.dout + (size_t)bh * sq * D;
-    const uint16_t* __restrict__ K = (const uint16_t*)p.k + (size_t)bh * sk * D;
-    const uint16_t* __restrict__ V = (const uint16_t*)p.v + (size_t)bh * sk * D;
+    const uint16_t* __restrict__ Q = (const uint16_t*)p.q + sl.q0 * D;
+    const uint16_t* __restrict__ dO = (const uint16_t*)p.dout + sl.q0 * D;
+    const uint16_t* __restrict__ K = (const uint16_t*)p.k + sl.k0 * D;
+    const uint16_t* __restrict__ V = (const uint16_t*)p.v + sl.k0 * D;
 
     // this wave's queries: B operands of S^T = K Q^T and dP^T = V dO^T (lane =
     // query); rows past the end re-read the last row and are never stored
@@ -556,8 +579,8 @@ fa_bwd_dq(BwdParams p)
         qf[kk] = *(const u32x4_t*)(Q + (size_t)qr * D + 16 * kk + 8 * g);
         gf[kk] = *(const u32x4_t*)(dO + (size_t)qr * D + 16 * kk + 8 * g);
     }
-    const float lse2 = p.lse[(size_t)bh * sq + qr] * kLog2e;
-    const float drow = p.dvec[(size_t)bh * sq + qr];
+    const float lse2 = p.lse[sl.q0 + qr] * kLog2e;
+    const float drow = p.dvec[sl.q0 + qr];
 
     const int q_end = min(q0 + BM, sq);
     const int kv_end = CAUSAL ? min(q_end, sk) : sk;
@@ -693,7 +716,7 @@ fa_bwd_dq(BwdParams p)
     if (t < nkv) step(Stage<0>{}, t);
 
     if (qrow < sq) {
-        uint16_t* dqrow = (uint16_t*)p.dq + ((size_t)bh * sq + qrow) * D;
+        uint16_t* dqrow = (uint16_t*)p.dq + (sl.q0 + qrow) * D;
         const float sc = p.scale;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
@@ -717,8 +740,15 @@ template <int D, bool BF16>
 hipError_t launch_bwd_t(BwdParams p, hipStream_t s)
 {
     constexpr int RPB = 256 / (D / 8);
-    const int64_t rows = (int64_t)p.bh * p.sq;
-    hipLaunchKernelGGL((fa_bwd_dot<D, BF16>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, s, p);
+    // D over every row of dout and o: a variable-length batch's packed rows
+    // are h * total_q rows of the same [.][D] layout
+    BwdParams pd = p;
+    if (p.cu_q) {
+        pd.bh = p.bh / p.batch;
+        pd.sq = p.total_q;
+    }
+    const int64_t rows = (int64_t)pd.bh * pd.sq;
+    hipLaunchKernelGGL((fa_bwd_dot<D, BF16>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, s, pd);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
 

@@ -58,6 +58,14 @@ struct BwdParams {
     int causal;
     int items_per_head;  // set per kernel by the launcher
     int n_items;
+    // variable-length batches (fa_bwd_varlen): [batch + 1] device offsets of
+    // each sequence's rows within a head's packed rows, or null for the dense
+    // layout.  With them bh counts (head, sequence) pairs, sq and sk are the
+    // longest lengths (grid sizes only) and total_q / total_k the packed rows.
+    const int32_t* cu_q;
+    const int32_t* cu_k;
+    int batch;
+    int total_q, total_k;
 };
 
 // FP8 forward launch parameters (fa_fwd_fp8).

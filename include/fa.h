@@ -275,6 +275,46 @@ FA_API int fa_bwd(const void* q, const void* k, const void* v, const void* o,
 FA_API size_t fa_bwd_workspace_bytes(int64_t b, int64_t h, int64_t sq);
 
 /*
+ * fa_bwd_varlen -- fa_bwd over a batch of packed sequences of different
+ * lengths, the gradients of fa_fwd_varlen (page "05 · kernel 工程与四代演化",
+ * section 6.1, lists the variable-length backward among the exported entry
+ * points).  Layout as fa_fwd_varlen, per head the sequences back to back:
+ *
+ *   q, o, dout, dq   [h, total_q, d] contiguous, dtype; sequence i owns rows
+ *                    cu_seqlens_q[i] .. cu_seqlens_q[i+1]-1 of every head
+ *   k, v, dk, dv     [h, total_k, d] contiguous, dtype; sequence i owns rows
+ *                    cu_seqlens_k[i] .. cu_seqlens_k[i+1]-1
+ *   lse              [h, total_q] fp32, as fa_fwd_varlen wrote it (o too)
+ *   workspace        at least fa_bwd_workspace_bytes(1, h, total_q) bytes,
+ *                    16-byte aligned, owned by the caller (holds D)
+ *   cu_seqlens_q, cu_seqlens_k  device int32 arrays of batch + 1 offsets,
+ *                    starting at 0, non-decreasing, ending at total_q /
+ *                    total_k
+ *   max_sq, max_sk   upper bounds of the query and key lengths (set the
+ *                    grids; rows and keys of a sequence past them are not
+ *                    computed)
+ *   d                64 or 128;  dtype FA_F16 or FA_BF16
+ *
+ * Each sequence's gradients are those of fa_bwd for that sequence alone
+ * (causal: local key j attends to local query r iff j <= r).  The keys of a
+ * sequence with no query rows get dk = dv = 0; the rows of a sequence with no
+ * keys get dq = 0 (fa_fwd_varlen leaves their o and lse unwritten, so pass
+ * any finite values there).  The offset arrays live on the device and are
+ * not checked on the host; the kernels clamp them into [0, total] so
+ * malformed offsets cannot address outside the buffers (the results are then
+ * unspecified).  Same rounding, determinism, overlap rules and status codes
+ * as fa_bwd.
+ */
+FA_API int fa_bwd_varlen(const void* q, const void* k, const void* v,
+                         const void* o, const void* dout, const float* lse,
+                         void* dq, void* dk, void* dv, void* workspace,
+                         size_t workspace_bytes, const int32_t* cu_seqlens_q,
+                         const int32_t* cu_seqlens_k, int64_t batch, int64_t h,
+                         int64_t total_q, int64_t total_k, int64_t max_sq,
+                         int64_t max_sk, int64_t d, float scale, int causal,
+                         int dtype, void* stream);
+
+/*
  * fa_fwd_fp8 -- the forward with FP8 inputs (page "05 · kernel 工程与四代演化",
  * section 4.4, describes the FP8 forward and its exponent-range trick).
  * Computes the attention of the dequantized tensors

@@ -31,7 +31,7 @@ def test_header_declares_the_entry_points():
     assert set(declared_symbols()) == {"fa_fwd", "fa_fwd_split", "fa_fwd_split_noalloc", "fa_query_launch",
                                        "fa_split_workspace_bytes",
                                        "fa_fwd_varlen", "fa_query_config", "fa_last_error",
-                                       "fa_version", "fa_bwd", "fa_bwd_workspace_bytes",
+                                       "fa_version", "fa_bwd", "fa_bwd_workspace_bytes", "fa_bwd_varlen",
                                        "fa_fwd_fp8", "fa_clock_probe"}
 
 
@@ -276,6 +276,42 @@ def call_bwd(**kw):
 def test_bwd_invalid_arguments_rejected_before_launch(kw, code):
     assert call_bwd(**kw) == code
     assert fa.fa_last_error().startswith("fa_bwd")
+
+
+def call_bwd_varlen(**kw):
+    args = dict(q=Q, k=K, v=V, o=O, dout=DO, lse=L, dq=DQ, dk=DK, dv=DV, workspace=WS,
+                workspace_bytes=1 << 30, cu_seqlens_q=CQ, cu_seqlens_k=CK, batch=3, h=2, total_q=100,
+                total_k=120, max_sq=50, max_sk=60, d=128, scale=0.125, causal=1, dtype=fa.FA_BF16,
+                stream=None)
+    args.update(kw)
+    return fa.fa_bwd_varlen(**args)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), fa.FA_ERR_INVALID_ARG),
+    (dict(dout=0), fa.FA_ERR_INVALID_ARG),
+    (dict(workspace=0), fa.FA_ERR_INVALID_ARG),
+    (dict(cu_seqlens_q=0), fa.FA_ERR_INVALID_ARG),
+    (dict(cu_seqlens_k=0), fa.FA_ERR_INVALID_ARG),
+    (dict(batch=0), fa.FA_ERR_INVALID_ARG),
+    (dict(total_q=0), fa.FA_ERR_INVALID_ARG),
+    (dict(max_sk=0), fa.FA_ERR_INVALID_ARG),
+    (dict(max_sq=101), fa.FA_ERR_INVALID_ARG),
+    (dict(max_sk=121), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), fa.FA_ERR_INVALID_ARG),
+    (dict(causal=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(dtype=fa.FA_F32), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=256), fa.FA_ERR_UNSUPPORTED),
+    (dict(dk=DK + 8), fa.FA_ERR_MISALIGNED),
+    (dict(cu_seqlens_k=CK + 2), fa.FA_ERR_MISALIGNED),
+    (dict(workspace_bytes=2 * 100 * 4 - 1), fa.FA_ERR_INVALID_ARG),   # one byte short of h * total_q * 4
+    (dict(dq=O), fa.FA_ERR_INVALID_ARG),                               # output over an input
+    (dict(workspace=DV + 256), fa.FA_ERR_INVALID_ARG),                 # workspace inside dv
+    (dict(total_q=1 << 24, max_sq=16), fa.FA_ERR_TOO_LARGE),
+])
+def test_bwd_varlen_invalid_arguments_rejected_before_launch(kw, code):
+    assert call_bwd_varlen(**kw) == code
+    assert fa.fa_last_error().startswith("fa_bwd_varlen")
 
 
 def test_bwd_binding_rejects_cpu_tensors():

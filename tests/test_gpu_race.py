@@ -9,7 +9,7 @@ compared with the fp64 oracle element by element, exactly as in the parity
 tests.  The shapes cover every kernel that copies into LDS: the 8-wave
 ping-pong forward (per-item and persistent grids, causal, ragged, sq != sk),
 the 4-wave forward (d = 64, 128, 256), split-KV, variable-length sequences,
-the backward and the FP8 forward.  The number of waves per workgroup is varied
+the backward (dense and variable-length) and the FP8 forward.  The number of waves per workgroup is varied
 by the shapes themselves (4 and 8 waves run the same tiles), and
 test_gpu_parity compares the two bit for bit on shared rows.
 """
@@ -21,6 +21,7 @@ import pytest
 import exact_attention_86_amd as fa
 import workloads as W
 from tests import test_gpu_bwd as B
+from tests import test_gpu_bwd_varlen as BV
 from tests import test_gpu_fp8 as F8
 from tests import test_gpu_parity as P
 
@@ -66,6 +67,11 @@ def test_poisoned_backward(gpu):
         B.test_bwd_matches_oracle(("bf16", 1, 2, 300, 300, True, None))
         B.test_bwd_matches_oracle(("f16", 2, 2, 640, 384, False, 0.2))
         B.test_bwd_matches_oracle(("bf16", 1, 2, 300, 300, True, None, 64))
+
+
+def test_poisoned_backward_varlen(gpu):
+    with fa.poisoned():
+        BV.test_bwd_varlen_per_sequence(("bf16", 2, 128, True, [130, 257, 64], [130, 300, 64]))
 
 
 def test_poisoned_fp8(gpu):
