@@ -448,7 +448,7 @@ FA_API int fa_bwd(const void* q, const void* k, const void* v, const void* o, co
     if (!isfinite(scale)) return fail(FA_ERR_INVALID_ARG, "fa_bwd: scale must be finite");
     if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARG, "fa_bwd: causal must be 0 or 1");
     if (d > 4096 || !fa::bwd_supported(dtype, (int)d))
-        return fail(FA_ERR_UNSUPPORTED, "fa_bwd: fp16/bf16 with d = 64 or 128 only");
+        return fail(FA_ERR_UNSUPPORTED, "fa_bwd: fp16/bf16 with d = 64, 128 or 256 only");
     if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)dout | (uintptr_t)dq |
          (uintptr_t)dk | (uintptr_t)dv | (uintptr_t)workspace) & 15u)
         return fail(FA_ERR_MISALIGNED, "fa_bwd: tensors and workspace must be 16-byte aligned");
@@ -465,7 +465,7 @@ FA_API int fa_bwd(const void* q, const void* k, const void* v, const void* o, co
         snprintf(g_err, sizeof g_err, "fa_bwd: %s", why);
         return FA_ERR_INVALID_ARG;
     }
-    const int64_t items = b * h * ((std::max(sq, sk) + 127) / 128);
+    const int64_t items = b * h * ((std::max(sq, sk) + 127) / 128) * (d > 128 ? 2 : 1);
     if (items > lim - 8) return fail(FA_ERR_TOO_LARGE, "fa_bwd: too many tiles for one launch");
 
     fa::BwdParams p;
@@ -518,7 +518,7 @@ FA_API int fa_bwd_varlen(const void* q, const void* k, const void* v, const void
     if (!isfinite(scale)) return fail(FA_ERR_INVALID_ARG, "fa_bwd_varlen: scale must be finite");
     if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARG, "fa_bwd_varlen: causal must be 0 or 1");
     if (d > 4096 || !fa::bwd_supported(dtype, (int)d))
-        return fail(FA_ERR_UNSUPPORTED, "fa_bwd_varlen: fp16/bf16 with d = 64 or 128 only");
+        return fail(FA_ERR_UNSUPPORTED, "fa_bwd_varlen: fp16/bf16 with d = 64, 128 or 256 only");
     if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)dout | (uintptr_t)dq |
          (uintptr_t)dk | (uintptr_t)dv | (uintptr_t)workspace) & 15u)
         return fail(FA_ERR_MISALIGNED, "fa_bwd_varlen: tensors and workspace must be 16-byte aligned");
@@ -537,7 +537,7 @@ FA_API int fa_bwd_varlen(const void* q, const void* k, const void* v, const void
         snprintf(g_err, sizeof g_err, "fa_bwd_varlen: %s", why);
         return FA_ERR_INVALID_ARG;
     }
-    const int64_t items = h * batch * ((std::max(max_sq, max_sk) + 127) / 128);
+    const int64_t items = h * batch * ((std::max(max_sq, max_sk) + 127) / 128) * (d > 128 ? 2 : 1);
     if (items > lim - 8) return fail(FA_ERR_TOO_LARGE, "fa_bwd_varlen: too many tiles for one launch");
 
     fa::BwdParams p;

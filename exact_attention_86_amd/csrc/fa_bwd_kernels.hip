@@ -52,10 +52,12 @@ constexpr float kLog2e = 1.4426950408889634f;
 // 2-3, so the 4 rows of a transpose read fall in different 4-chunk groups.
 // 128-byte rows (CPR = 8): the row's parity already picks the half of a bank
 // line, and row bits 1-3 pick the chunk, so 16 rows cover all 16 positions.
+// 512-byte rows (CPR = 32) start on a bank line like 256-byte ones and take
+// the same map (it only moves a chunk within its 16-chunk half of the row).
 template <int CPR>
 __device__ __forceinline__ int swz_b(int row)
 {
-    if constexpr (CPR == 16) return ((row & 3) << 2) | ((row >> 2) & 3);
+    if constexpr (CPR >= 16) return ((row & 3) << 2) | ((row >> 2) & 3);
     return (row >> 1) & 7;
 }
 
@@ -132,14 +134,19 @@ template <int D, bool BF16, bool CAUSAL>
 __global__ void __launch_bounds__(256, 1)
 fa_bwd_dkdv(BwdParams p)
 {
-    static_assert(D == 64 || D == 128, "128- or 256-byte rows");
+    static_assert(D == 64 || D == 128 || D == 256, "128-, 256- or 512-byte rows");
     constexpr int CPR = D / 8;            // 16-byte chunks per row
     constexpr int NW = 4;                 // waves; wave w owns keys [32w, 32w+32)
     constexpr int BN = 32 * NW;           // keys per workgroup
     constexpr int BMQ = 64;               // queries per step (two 32-row blocks)
     constexpr int RB = D * 2;             // bytes per row
     constexpr int NKK = D / 16;           // k-steps of S and dP
-    constexpr int NDT = D / 32;           // 32-wide d tiles of dK^T, dV^T
+    // d = 256: a work item accumulates dK^T and dV^T for one half of d (the
+    // whole would take 256 registers per lane for the accumulators alone, and
+    // the K and V fragments another 128), recomputing S and dP in each half
+    constexpr int NSPLIT = D > 128 ? 2 : 1;
+    constexpr int DH = D / NSPLIT;        // d range of this item's dK, dV
+    constexpr int NDT = DH / 32;          // 32-wide d tiles of dK^T, dV^T
     constexpr int TQ = BMQ * RB;          // bytes of one Q or dO tile
     constexpr int OFF_LSE = 2 * TQ;       // stage layout: Q | dO | LSE (log2) | D
     constexpr int OFF_D = OFF_LSE + BMQ * 4;
@@ -150,6 +157,8 @@ fa_bwd_dkdv(BwdParams p)
 
     int bh, kt;
     if (!map_xcd_item(p.n_items, p.items_per_head, bh, kt)) return;
+    const int hd = kt % NSPLIT;           // which half of d (d = 256)
+    kt /= NSPLIT;
     const Slice sl = bwd_slice(p, bh);
     const int sq = sl.sq, sk = sl.sk;
     const int n0 = kt * BN;
@@ -252,7 +261,8 @@ fa_bwd_dkdv(BwdParams p)
         const int row = 8 * j + 4 * g + tr_r;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
-            rt[j][dt] = row * RB + (((4 * dt + 2 * half + (tr_c >> 1)) ^ swz_b<CPR>(row)) << 4) + (tr_c & 1) * 8;
+            rt[j][dt] = row * RB + (((hd * (DH / 8) + 4 * dt + 2 * half + (tr_c >> 1)) ^ swz_b<CPR>(row)) << 4) +
+                        (tr_c & 1) * 8;
     }
 
     f32x16_t dva[NDT], dka[NDT];
@@ -377,6 +387,7 @@ fa_bwd_dkdv(BwdParams p)
                                      : (I == 2 ? 5 : I == 7 ? 6 : I == 12 ? 7 : -1);
             if constexpr (C >= 0 && C < 2 * DMA) copy_one(Stage<S ^ 1>{}, Stage<C>{}, qn);
         };
+        if constexpr (D <= 128) {
         static_assert(2 * DMA <= 8, "copy slots for at most eight copies per wave per step");
         if (ok0 && ok1) {
             constexpr int KA = 4;
@@ -480,11 +491,14 @@ fa_bwd_dkdv(BwdParams p)
             });
             // ---- dV/dK of block 1 ----
             pv_stream(sb + 32 * RB, pp1, dsp1, [&](auto) {});
-        } else {
-            static_for<2 * DMA>([&](auto c) { copy_one(Stage<S ^ 1>{}, c, qn); });
-            if (ok0) compute_block(sb, 0, q0);
-            if (ok1) compute_block(sb, 1, q0 + 32);
+            return;
         }
+        }
+        // the simple form: one live block, or d = 256 (two blocks' scores and
+        // a stream's operand ring do not fit beside the K and V fragments)
+        static_for<2 * DMA>([&](auto c) { copy_one(Stage<S ^ 1>{}, c, qn); });
+        if (ok0) compute_block(sb, 0, q0);
+        if (ok1) compute_block(sb, 1, q0 + 32);
     };
 
     auto step = [&](auto st_tag, int t) {
@@ -518,7 +532,7 @@ fa_bwd_dkdv(BwdParams p)
         for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
             for (int rb = 0; rb < 4; ++rb) {
-                const int d0 = 32 * dt + 8 * rb + 4 * g;
+                const int d0 = hd * DH + 32 * dt + 8 * rb + 4 * g;
                 *(u32x2_t*)(dvrow + d0) = u32x2_t{pack2(dva[dt][4 * rb], dva[dt][4 * rb + 1], BF16),
                                                   pack2(dva[dt][4 * rb + 2], dva[dt][4 * rb + 3], BF16)};
                 *(u32x2_t*)(dkrow + d0) = u32x2_t{pack2(dka[dt][4 * rb] * sc, dka[dt][4 * rb + 1] * sc, BF16),
@@ -531,10 +545,12 @@ fa_bwd_dkdv(BwdParams p)
 // dQ: one workgroup per 128 queries of one head
 // ---------------------------------------------------------------------------
 template <int D, bool BF16, bool CAUSAL>
-__global__ void __launch_bounds__(256, 2)
+__global__ void __launch_bounds__(256, D > 128 ? 1 : 2)
 fa_bwd_dq(BwdParams p)
 {
-    static_assert(D == 64 || D == 128, "128- or 256-byte rows");
+    // d = 256: the Q and dO fragments (128 registers per lane) and the dQ^T
+    // accumulators (128) need one wave per SIMD
+    static_assert(D == 64 || D == 128 || D == 256, "128-, 256- or 512-byte rows");
     constexpr int CPR = D / 8;            // 16-byte chunks per row
     constexpr int NW = 4;                 // waves; wave w owns queries [32w, 32w+32)
     constexpr int BM = 32 * NW;           // queries per workgroup
@@ -752,7 +768,7 @@ hipError_t launch_bwd_t(BwdParams p, hipStream_t s)
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
 
-    p.items_per_head = (p.sk + 127) / 128;
+    p.items_per_head = (p.sk + 127) / 128 * (D > 128 ? 2 : 1);  // d = 256: two halves of d per key tile
     p.n_items = p.bh * p.items_per_head;
     auto dkdv = p.causal ? fa_bwd_dkdv<D, BF16, true> : fa_bwd_dkdv<D, BF16, false>;
     hipLaunchKernelGGL(dkdv, dim3(round8(p.n_items)), dim3(256), 0, s, p);
@@ -768,7 +784,7 @@ hipError_t launch_bwd_t(BwdParams p, hipStream_t s)
 
 }  // namespace
 
-bool bwd_supported(int dtype, int d) { return (dtype == 1 || dtype == 2) && (d == 64 || d == 128); }
+bool bwd_supported(int dtype, int d) { return (dtype == 1 || dtype == 2) && (d == 64 || d == 128 || d == 256); }
 
 hipError_t launch_bwd(int dtype, int d, const BwdParams& p, hipStream_t stream)
 {
@@ -778,6 +794,9 @@ hipError_t launch_bwd(int dtype, int d, const BwdParams& p, hipStream_t stream)
     } else if (d == 64) {
         if (dtype == 2) return launch_bwd_t<64, true>(p, stream);
         if (dtype == 1) return launch_bwd_t<64, false>(p, stream);
+    } else if (d == 256) {
+        if (dtype == 2) return launch_bwd_t<256, true>(p, stream);
+        if (dtype == 1) return launch_bwd_t<256, false>(p, stream);
     }
     return hipErrorInvalidValue;
 }

@@ -253,7 +253,7 @@ FA_API int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o,
  *                    caller; contents on entry do not matter.  Calls that
  *                    share a workspace must be ordered (same stream).
  *   workspace_bytes  its size in bytes
- *   d                64 or 128;  dtype FA_F16 or FA_BF16
+ *   d                64, 128 or 256;  dtype FA_F16 or FA_BF16
  *   scale, causal    as passed to fa_fwd
  *   stream           hipStream_t; three kernels are enqueued on it
  *
@@ -261,8 +261,8 @@ FA_API int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o,
  * P and dS are rounded to dtype before they enter the matrix cores (fp32
  * accumulation).  Deterministic: no atomics, the same inputs give the same
  * bits.  Returns FA_OK or an fa_status code as fa_fwd (FA_ERR_UNSUPPORTED for
- * fp32 or d other than 64 and 128; FA_ERR_INVALID_ARG for a missing, small or
- * overlapping workspace).
+ * fp32 or d other than 64, 128 and 256; FA_ERR_INVALID_ARG for a missing,
+ * small or overlapping workspace).
  */
 FA_API int fa_bwd(const void* q, const void* k, const void* v, const void* o,
                   const void* dout, const float* lse, void* dq, void* dk, void* dv,
@@ -293,7 +293,7 @@ FA_API size_t fa_bwd_workspace_bytes(int64_t b, int64_t h, int64_t sq);
  *   max_sq, max_sk   upper bounds of the query and key lengths (set the
  *                    grids; rows and keys of a sequence past them are not
  *                    computed)
- *   d                64 or 128;  dtype FA_F16 or FA_BF16
+ *   d                64, 128 or 256;  dtype FA_F16 or FA_BF16
  *
  * Each sequence's gradients are those of fa_bwd for that sequence alone
  * (causal: local key j attends to local query r iff j <= r).  The keys of a

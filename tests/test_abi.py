@@ -261,7 +261,7 @@ def call_bwd(**kw):
     (dict(causal=2), fa.FA_ERR_INVALID_ARG),
     (dict(dtype=fa.FA_F32), fa.FA_ERR_UNSUPPORTED),
     (dict(d=32), fa.FA_ERR_UNSUPPORTED),
-    (dict(d=256), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=512), fa.FA_ERR_UNSUPPORTED),
     (dict(dtype=9), fa.FA_ERR_UNSUPPORTED),
     (dict(dq=DQ + 8), fa.FA_ERR_MISALIGNED),
     (dict(workspace=WS + 4), fa.FA_ERR_MISALIGNED),
@@ -301,7 +301,7 @@ def call_bwd_varlen(**kw):
     (dict(scale=float("inf")), fa.FA_ERR_INVALID_ARG),
     (dict(causal=-1), fa.FA_ERR_INVALID_ARG),
     (dict(dtype=fa.FA_F32), fa.FA_ERR_UNSUPPORTED),
-    (dict(d=256), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
     (dict(dk=DK + 8), fa.FA_ERR_MISALIGNED),
     (dict(cu_seqlens_k=CK + 2), fa.FA_ERR_MISALIGNED),
     (dict(workspace_bytes=2 * 100 * 4 - 1), fa.FA_ERR_INVALID_ARG),   # one byte short of h * total_q * 4

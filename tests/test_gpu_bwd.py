@@ -88,7 +88,17 @@ CASES_D64 = [
 ]
 
 
-@pytest.mark.parametrize("case", CASES + CASES_D64, ids=lambda c: "%s_b%dh%d_sq%d_sk%d_%s_%s_d%d" % (
+# d = 256: dK and dV accumulated in two halves of d, one wave per SIMD
+CASES_D256 = [
+    ("bf16", 1, 2, 128, 128, True, None, 256),
+    ("f16", 1, 2, 200, 328, False, None, 256),
+    ("bf16", 2, 2, 333, 150, True, None, 256),
+    ("f16", 1, 1, 1, 77, False, None, 256),
+    ("bf16", 1, 2, 190, 140, False, -0.07, 256),
+]
+
+
+@pytest.mark.parametrize("case", CASES + CASES_D64 + CASES_D256, ids=lambda c: "%s_b%dh%d_sq%d_sk%d_%s_%s_d%d" % (
     c[0], c[1], c[2], c[3], c[4], "causal" if c[5] else "full", c[6], c[7] if len(c) > 7 else 128))
 def test_bwd_matches_oracle(case):
     dtype, b, h, sq, sk, causal, scale = case[:7]

@@ -33,6 +33,7 @@ CASES = [
     ("f16", 2, 128, True, [77, 200, 1], [1, 333, 129]),
     ("bf16", 1, 64, False, [129, 128, 127, 300], [129, 128, 127, 40]),
     ("bf16", 2, 128, False, [50, 40], [60, 0]),
+    ("f16", 2, 256, True, [200, 3, 129], [250, 3, 300]),
 ]
 
 

@@ -67,6 +67,7 @@ def test_poisoned_backward(gpu):
         B.test_bwd_matches_oracle(("bf16", 1, 2, 300, 300, True, None))
         B.test_bwd_matches_oracle(("f16", 2, 2, 640, 384, False, 0.2))
         B.test_bwd_matches_oracle(("bf16", 1, 2, 300, 300, True, None, 64))
+        B.test_bwd_matches_oracle(("f16", 1, 2, 300, 260, True, None, 256))
 
 
 def test_poisoned_backward_varlen(gpu):
