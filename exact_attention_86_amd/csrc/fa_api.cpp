@@ -72,9 +72,9 @@ struct Launch {
 };
 
 // the per-item launch (host arithmetic only, no HIP call)
-bool plan_launch(int dtype, int64_t d, int causal, int64_t b, int64_t h, int64_t sq, Launch* L)
+bool plan_launch(int dtype, int64_t d, int causal, int64_t b, int64_t h, int64_t sq, int64_t sk, Launch* L)
 {
-    if (!fa::tile_config(dtype, (int)d, b * h, sq, causal, &L->tc)) return false;
+    if (!fa::tile_config(dtype, (int)d, b * h, sq, sk, causal, &L->tc)) return false;
     // causal work items pair query tile nQ-1-i with tile i (equal cost)
     L->n_mtiles = (sq + L->tc.block_m - 1) / L->tc.block_m;
     L->items_per_head = causal ? (L->n_mtiles + 1) / 2 : L->n_mtiles;
@@ -118,7 +118,7 @@ FA_API int fa_query_config(int dtype, int64_t d, int causal, int64_t b, int64_t 
     if (b <= 0 || h <= 0 || sq <= 0 || sk <= 0 || (causal != 0 && causal != 1))
         return fail(FA_ERR_INVALID_ARG, "fa_query_config: sizes must be >= 1, causal 0 or 1");
     fa::TileConfig tc;
-    if (d <= 0 || d > 4096 || !fa::tile_config(dtype, (int)d, b * h, sq, causal, &tc))
+    if (d <= 0 || d > 4096 || !fa::tile_config(dtype, (int)d, b * h, sq, sk, causal, &tc))
         return fail(FA_ERR_UNSUPPORTED, "fa_query_config: dtype/head size not served");
     if (block_m) *block_m = tc.block_m;
     if (block_n) *block_n = tc.block_n;
@@ -136,7 +136,7 @@ FA_API int fa_query_launch(int dtype, int64_t d, int causal, int64_t b, int64_t 
     if (b > INT32_MAX || h > INT32_MAX || sq > INT32_MAX || b * h > INT32_MAX)
         return fail(FA_ERR_TOO_LARGE, "fa_query_launch: too many tiles for one launch");
     Launch L;
-    if (d <= 0 || d > 4096 || !plan_launch(dtype, d, causal, b, h, sq, &L))
+    if (d <= 0 || d > 4096 || !plan_launch(dtype, d, causal, b, h, sq, sk, &L))
         return fail(FA_ERR_UNSUPPORTED, "fa_query_launch: dtype/head size not served");
     if (launch_too_large(L, b * h))
         return fail(FA_ERR_TOO_LARGE, "fa_query_launch: too many tiles for one launch");
@@ -220,7 +220,7 @@ FA_API int fa_fwd(const void* q, const void* k, const void* v, void* o, float* l
     const int rc = check_common("fa_fwd", q, k, v, o, lse, b, h, sq, sk, d, scale, causal, dtype, &p);
     if (rc != FA_OK) return rc;
     Launch L;
-    if (!plan_launch(dtype, d, causal, b, h, sq, &L))
+    if (!plan_launch(dtype, d, causal, b, h, sq, sk, &L))
         return fail(FA_ERR_UNSUPPORTED, "fa_fwd: head size not served for this dtype");
     if (launch_too_large(L, b * h)) return fail(FA_ERR_TOO_LARGE, "fa_fwd: too many tiles for one launch");
     maybe_persist(&L, b * h, causal);  // every argument is valid: the runtime may be asked now

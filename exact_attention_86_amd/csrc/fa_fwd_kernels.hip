@@ -155,8 +155,14 @@ struct VRead {
 // fp32 to the workspace, and fa_combine merges the parts.
 // VARLEN: packed variable-length sequences; a work item is one query tile of
 // one sequence of one head, and every address is offset to that sequence.
-template <int D, int BN, int NW, int QB, bool BF16, bool CAUSAL, bool SPLIT, bool VARLEN = false>
-__global__ void __launch_bounds__(NW * 64, QB == 1 ? 2 : 1)
+// KG = 2: two key groups of NW waves share the tile's query rows; group g
+// takes key tiles g, g + 2, ... through its own LDS stages (both groups step
+// through the same barriers), and at the end group 1 hands its unnormalised
+// O, running max and row sum to group 0 through LDS, which merges them.  For
+// problems with fewer work items than CUs: each wave walks half the key tiles
+// and every SIMD holds two waves.
+template <int D, int BN, int NW, int QB, bool BF16, bool CAUSAL, bool SPLIT, bool VARLEN = false, int KG = 1>
+__global__ void __launch_bounds__(NW * KG * 64, QB == 1 && KG == 1 ? 2 : 1)
 fa_fwd_16(Params p)
 {
     constexpr int BM = NW * 32 * QB;     // query rows per workgroup tile
@@ -173,16 +179,21 @@ fa_fwd_16(Params p)
     constexpr int NKR = NKK < 8 ? NKK : 8;  // distinct K-read lane offsets
     static_assert(CPR >= 8, "swizzles need at least 8 chunks per row");
     static_assert(DMA >= 1 && NCH % (64 * NW) == 0, "tile must split evenly over waves");
-    static_assert(2 * 2 * TB <= 160 * 1024, "LDS budget");
+    static_assert(KG * 2 * 2 * TB <= 160 * 1024, "LDS budget");
+    static_assert(KG == 1 || (KG == 2 && QB == 1 && !SPLIT && !VARLEN), "key groups: plain one-block tiles only");
+    constexpr int GROUP_BYTES = 2 * 2 * TB;  // one key group's two stages
 
-    // [stage][0 = K, 1 = V][BN rows x D], rows row-major with swizzled chunks
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][TILE];
+    // [key group][stage][0 = K, 1 = V][BN rows x D], rows row-major with
+    // swizzled chunks
+    __shared__ __attribute__((aligned(16))) uint16_t lds[KG][2][2][TILE];
 
     int bh, item;
     if (!map_item(p, bh, item)) return;
 
     const int tid = threadIdx.x;
-    const int w = tid >> 6;
+    // (both wave-uniform; said so, so that every branch on them is uniform)
+    const int kg = KG > 1 ? __builtin_amdgcn_readfirstlane((tid >> 6) / NW) : 0;  // key group
+    const int w = KG > 1 ? __builtin_amdgcn_readfirstlane((tid >> 6) % NW) : tid >> 6;  // wave within it
     const int lane = tid & 63;
     const int l32 = lane & 31;
     const int g = lane >> 5;
@@ -224,7 +235,7 @@ fa_fwd_16(Params p)
         dk[j] = row * RB + ((pch ^ swz_k<CPR>(row)) << 4);
         dv[j] = row * RB + ((pch ^ swz_v<CPR>(row)) << 4);
     }
-    const uint32_t lds0 = lds_addr(&lds[0][0][0]);
+    const uint32_t lds0 = lds_addr(&lds[0][0][0][0]) + kg * GROUP_BYTES;
     // copy j of K or V for the tile at n0 into stage `stage`.  full: the tile
     // lies inside [0, sk) and the precomputed offsets apply; otherwise rows
     // past the last key re-read the last key (finite data; those keys' scores
@@ -272,7 +283,7 @@ fa_fwd_16(Params p)
     //  K (S^T A operand): row kb*32 + l32, logical chunk 2kk + g
     uint32_t rk[NKR];
 #pragma unroll
-    for (int kk = 0; kk < NKR; ++kk) rk[kk] = l32 * RB + (((2 * kk + g) ^ swz_k<CPR>(l32)) << 4);
+    for (int kk = 0; kk < NKR; ++kk) rk[kk] = kg * GROUP_BYTES + l32 * RB + (((2 * kk + g) ^ swz_k<CPR>(l32)) << 4);
     //  V (O^T A operand, transpose reads): lane 4r + c of its 16-lane group
     //  reads key row 16kc + 8j + 4g + r, d = 32dt + 16*half + 4c
     const int sub = lane & 15, vr = sub >> 2, vc = sub & 3, vhalf = (lane >> 4) & 1;
@@ -280,7 +291,7 @@ fa_fwd_16(Params p)
     constexpr int NRV = VRead<CPR>::NRV < NDT ? VRead<CPR>::NRV : NDT;
     uint32_t rv[NRV];
 #pragma unroll
-    for (int e = 0; e < NRV; ++e) rv[e] = TB + VRead<CPR>::offset(e, v_row, vhalf, vc);
+    for (int e = 0; e < NRV; ++e) rv[e] = kg * GROUP_BYTES + TB + VRead<CPR>::offset(e, v_row, vhalf, vc);
 
     auto process = [&](const int mt, const int split) {
         const int q0 = mt * BM;
@@ -333,8 +344,8 @@ fa_fwd_16(Params p)
         auto compute = [&](auto stage_tag, auto full_tag, int n0) {
             constexpr int S = decltype(stage_tag)::value;
             constexpr bool PF_FULL = decltype(full_tag)::value;
-            const char* sb = (const char*)&lds[S][0][0];
-            const int nn = n0 + BN;  // prefetched tile
+            const char* sb = (const char*)&lds[0][S][0][0];  // the key group's offset is in rk, rv
+            const int nn = n0 + KG * BN;  // prefetched tile (this key group's next)
 
             // ---- S^T = K Q^T on the matrix cores (each K read feeds QB) ----
             f32x16_t s[QB][NKB];
@@ -357,19 +368,28 @@ fa_fwd_16(Params p)
                     });
             }
 
-            // ---- masks: ragged key tail, causal diagonal ----
+            // ---- masks: ragged key tail, causal diagonal.  Score r of block kb
+            //      is key n0 + 32kb + 4g + off(r); it lives iff key <= lim =
+            //      min(sk - 1, qrow) (causal) or sk - 1, so the sign of
+            //      lim - key selects -inf with a mask and a bit-field insert (no
+            //      per-element compare: their lane masks would take scalar
+            //      registers) ----
             const bool need_mask = (n0 + BN > sk) || (CAUSAL && n0 + BN - 1 > wq_first);
             if (need_mask) {
 #pragma unroll
-                for (int qb = 0; qb < QB; ++qb)
+                for (int qb = 0; qb < QB; ++qb) {
+                    const int lim0 = (CAUSAL ? min(sk - 1, qrow[qb]) : sk - 1) - n0 - 4 * g;
 #pragma unroll
                     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
                         for (int r = 0; r < 16; ++r) {
-                            const int key = n0 + kb * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
-                            const bool dead = (key >= sk) || (CAUSAL && key > qrow[qb]);
-                            if (dead) s[qb][kb][r] = -INFINITY;
+                            const int off = kb * 32 + (r >> 2) * 8 + (r & 3);
+                            const uint32_t dead = (uint32_t)((lim0 - off) >> 31);
+                            const float x = s[qb][kb][r];  // through a scalar: a bit cast of a vector element reads element 0
+                            const uint32_t bits = __builtin_bit_cast(uint32_t, x);
+                            s[qb][kb][r] = __builtin_bit_cast(float, (bits & ~dead) | (0xff800000u & dead));
                         }
+                }
             }
 
             // ---- online softmax (log2 units) ----
@@ -466,28 +486,69 @@ fa_fwd_16(Params p)
         };
 
         // one key tile: publish its stage, then compute (the stage index is a
-        // template constant so every LDS offset is an immediate)
+        // template constant so every LDS offset is an immediate).  Key group
+        // kg takes tiles t_lo + kg, t_lo + kg + KG, ...; every group runs the
+        // same number of steps (a group past its last tile only joins the
+        // barrier)
         auto step = [&](auto stage_tag, int t) {
             constexpr int S = decltype(stage_tag)::value;
             wait_copies();
             __syncthreads();
-            const bool pf = t + 1 < t_hi;
-            const bool pf_full = pf && (t + 2) * BN <= sk;
+            const bool pf = t + KG < t_hi;
+            const bool pf_full = pf && (t + KG + 1) * BN <= sk;
             if (t < w_nkv && pf_full) {
                 compute(stage_tag, Stage<1>{}, t * BN);
             } else {
-                if (pf) issue_tile(Stage<S ^ 1>{}, (t + 1) * BN);
-                if (t < w_nkv) compute(stage_tag, Stage<0>{}, t * BN);
+                if (pf) issue_tile(Stage<S ^ 1>{}, (t + KG) * BN);
+                if (t < w_nkv && t < t_hi) compute(stage_tag, Stage<0>{}, t * BN);
             }
         };
 
-        if (t_lo < t_hi) issue_tile(Stage<0>{}, t_lo * BN);
-        int t = t_lo;
-        for (; t + 1 < t_hi; t += 2) {
-            step(Stage<0>{}, t);
-            step(Stage<1>{}, t + 1);
+        const int g_lo = t_lo + kg;
+        const int nsteps = (t_hi - t_lo + KG - 1) / KG;
+        if (g_lo < t_hi) issue_tile(Stage<0>{}, g_lo * BN);
+        int i = 0;
+        for (; i + 1 < nsteps; i += 2) {
+            step(Stage<0>{}, g_lo + i * KG);
+            step(Stage<1>{}, g_lo + (i + 1) * KG);
         }
-        if (t < t_hi) step(Stage<0>{}, t);
+        if (i < nsteps) step(Stage<0>{}, g_lo + i * KG);
+
+        if constexpr (KG > 1) {
+            // ---- merge the key groups: group 1 parks its unnormalised O^T,
+            //      running max and partial row sum in LDS (lane-major, so group
+            //      0's wave w reads them back in its own register layout), and
+            //      group 0 rescales both to the larger max and adds.  A group
+            //      that saw no key of a row has m = -inf, l = 0, O = 0 and
+            //      weight 0. ----
+            constexpr int NR = NDT * 16;  // accumulator registers per lane
+            static_assert(NW * (NR + 2) * 64 * 4 <= KG * GROUP_BYTES, "merge buffer inside the stages");
+            float* mb = (float*)&lds[0][0][0][0] + (size_t)w * (NR + 2) * 64;
+            __syncthreads();  // every wave is done with the stages
+            if (kg == 1) {
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) mb[(dt * 16 + r) * 64 + lane] = oacc[0][dt][r];
+                mb[NR * 64 + lane] = m_run[0];
+                mb[(NR + 1) * 64 + lane] = l_run[0];
+            }
+            __syncthreads();
+            if (kg == 1) return;  // group 0 writes the tile
+            const float m1 = mb[NR * 64 + lane], l1 = mb[(NR + 1) * 64 + lane];
+            const float m = fmaxf(m_run[0], m1);
+            const float a0 = m_run[0] == -INFINITY ? 0.f : fast_exp2(m_run[0] - m);
+            const float a1 = m1 == -INFINITY ? 0.f : fast_exp2(m1 - m);
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    oacc[0][dt][r] = __builtin_fmaf(oacc[0][dt][r], a0, mb[(dt * 16 + r) * 64 + lane] * a1);
+                __builtin_amdgcn_sched_barrier(0);  // one d tile's loads at a time
+            }
+            l_run[0] = __builtin_fmaf(l_run[0], a0, l1 * a1);
+            m_run[0] = m;
+        }
 
         // ---- epilogue: O = O^T / l, LSE = (m + log2 l) ln 2 ----
         if constexpr (SPLIT) {
@@ -1232,6 +1293,14 @@ static hipError_t launch16(const Params& p, hipStream_t s)
     return launch(fa_fwd_16<D, BN, NW, QB, BF16, false, false>, NW, p, s);
 }
 
+// the 4-wave kernel with two key groups (8 waves per workgroup)
+template <int D, int BN, bool BF16>
+static hipError_t launch16kg(const Params& p, hipStream_t s)
+{
+    if (p.causal) return launch(fa_fwd_16<D, BN, 4, 1, BF16, true, false, false, 2>, 8, p, s);
+    return launch(fa_fwd_16<D, BN, 4, 1, BF16, false, false, false, 2>, 8, p, s);
+}
+
 // variable-length sequences (4-wave kernel)
 template <int D, int BN, bool BF16>
 static hipError_t launch16varlen(const Params& p, hipStream_t s)
@@ -1275,7 +1344,11 @@ static hipError_t launch32(const Params& p, hipStream_t s)
 // exactly these values.  fp16/bf16 with d = 128 uses the ping-pong kernel
 // (256-row tiles, one 8-wave workgroup per CU) when the problem has at least
 // one work item per CU, else the 4-wave kernel (128-row tiles, two per CU).
-bool tile_config(int dtype, int d, int64_t bh, int64_t sq, int causal, TileConfig* tc)
+// When even the 4-wave kernel's work items (128-row tiles, causal pairs)
+// number fewer than the CUs and each tile sees at least 4 key tiles, d = 64
+// and d = 128 take the 4-wave kernel with two key groups: 8 waves per
+// workgroup, each walking half of the tile's keys.
+bool tile_config(int dtype, int d, int64_t bh, int64_t sq, int64_t sk, int causal, TileConfig* tc)
 {
     constexpr int64_t kCUs = 256;
     int bn = 0, nw = 0, qb = 1, lds = 0, kind = 0;
@@ -1293,6 +1366,15 @@ bool tile_config(int dtype, int d, int64_t bh, int64_t sq, int causal, TileConfi
             return false;
         }
         lds = 4 * bn * d * 2;
+        if (kind == 0 && d <= 128) {
+            const int64_t nq = (sq + 127) / 128;
+            const int64_t items = bh * (causal ? (nq + 1) / 2 : nq);
+            if (items < kCUs && (sk + bn - 1) / bn >= 4) {
+                nw = 8;  // two key groups of 4 waves over 128-row tiles
+                kind = 3;
+                lds *= 2;
+            }
+        }
     } else if (dtype == 0) {
         if (d == 64)       { bn = 32; nw = 2; }
         else if (d == 128) { bn = 32; nw = 2; }
@@ -1301,7 +1383,7 @@ bool tile_config(int dtype, int d, int64_t bh, int64_t sq, int causal, TileConfi
     } else {
         return false;
     }
-    tc->block_m = nw * 32 * qb;
+    tc->block_m = (kind == 3 ? 4 : nw) * 32 * qb;
     tc->block_n = bn;
     tc->waves = nw;
     tc->lds = lds;
@@ -1367,13 +1449,19 @@ hipError_t launch_fwd(int dtype, int d, const TileConfig& tc, const Params& p, h
 {
     switch (dtype) {
     case 2:
-        if (d == 64) return launch16<64, 128, 4, 1, true>(p, s);
-        if (d == 128) return tc.kind ? launch16pp<128, 64, true>(p, tc.kind == 2, s) : launch16<128, 64, 4, 1, true>(p, s);
+        if (d == 64) return tc.kind == 3 ? launch16kg<64, 128, true>(p, s) : launch16<64, 128, 4, 1, true>(p, s);
+        if (d == 128) {
+            if (tc.kind == 1 || tc.kind == 2) return launch16pp<128, 64, true>(p, tc.kind == 2, s);
+            return tc.kind == 3 ? launch16kg<128, 64, true>(p, s) : launch16<128, 64, 4, 1, true>(p, s);
+        }
         if (d == 256) return launch16<256, 32, 4, 1, true>(p, s);
         break;
     case 1:
-        if (d == 64) return launch16<64, 128, 4, 1, false>(p, s);
-        if (d == 128) return tc.kind ? launch16pp<128, 64, false>(p, tc.kind == 2, s) : launch16<128, 64, 4, 1, false>(p, s);
+        if (d == 64) return tc.kind == 3 ? launch16kg<64, 128, false>(p, s) : launch16<64, 128, 4, 1, false>(p, s);
+        if (d == 128) {
+            if (tc.kind == 1 || tc.kind == 2) return launch16pp<128, 64, false>(p, tc.kind == 2, s);
+            return tc.kind == 3 ? launch16kg<128, 64, false>(p, s) : launch16<128, 64, 4, 1, false>(p, s);
+        }
         if (d == 256) return launch16<256, 32, 4, 1, false>(p, s);
         break;
     case 0:

@@ -36,7 +36,8 @@ struct TileConfig {
     int block_m, block_n, waves, lds;
     int qb;    // 32-row query blocks per wave
     int kind;  // 0: one wave group; 1: two ping-pong wave groups, one workgroup per
-               // work item; 2: the same kernel on a persistent grid (fa_fwd sets it)
+               // work item; 2: the same kernel on a persistent grid (fa_fwd sets it);
+               // 3: one wave group per half of the key tiles (two key groups)
 };
 
 // Backward launch parameters (fa_bwd).
@@ -84,7 +85,7 @@ struct Fp8Params {
     int n_items;
 };
 
-bool tile_config(int dtype, int d, int64_t bh, int64_t sq, int causal, TileConfig* tc);
+bool tile_config(int dtype, int d, int64_t bh, int64_t sq, int64_t sk, int causal, TileConfig* tc);
 hipError_t launch_fwd(int dtype, int d, const TileConfig& tc, const Params& p, hipStream_t stream);
 bool tile_config_split(int dtype, int d, TileConfig* tc);
 hipError_t launch_fwd_varlen(int dtype, int d, const Params& p, hipStream_t stream);

@@ -92,7 +92,8 @@ FA_API int fa_fwd(const void* q, const void* k, const void* v, void* o,
  * b, h, sq, sk); the choice of kernel may depend on the sizes.
  *   block_m  query rows per workgroup tile
  *   block_n  keys per inner step (one K/V tile through LDS)
- *   waves    wavefronts per workgroup (64 lanes each)
+ *   waves    wavefronts per workgroup (64 lanes each; 8 with block_m 128
+ *            means two groups of 4 waves that split the key tiles)
  *   lds      LDS bytes per workgroup
  * Any output pointer may be NULL.  Returns FA_OK, FA_ERR_INVALID_ARG (a size
  * below 1, causal not 0/1) or FA_ERR_UNSUPPORTED.  Host only; no HIP call.

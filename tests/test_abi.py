@@ -51,7 +51,7 @@ def test_version():
                                      (fa.FA_F32, 64), (fa.FA_F32, 128)])
 def test_query_config_served(dtype, d):
     cfg = fa.fa_query_config(dtype, d, 1)
-    assert cfg["block_m"] % (32 * cfg["waves"]) == 0
+    assert cfg["block_m"] % 32 == 0 and cfg["waves"] in (2, 4, 8)
     assert cfg["block_n"] % 32 == 0
     assert 0 < cfg["lds"] <= 160 * 1024
 
@@ -60,8 +60,18 @@ def test_query_config_depends_on_size():
     # d = 128 16-bit: 256-row ping-pong tiles when there is a work item per CU
     big = fa.fa_query_config(fa.FA_BF16, 128, 1, 4, 32, 4096, 4096)
     assert (big["block_m"], big["waves"]) == (256, 8)
+    # fewer 128-row work items than CUs: two key groups of 4 waves per tile
     small = fa.fa_query_config(fa.FA_F16, 128, 0, 2, 8, 1024, 1024)
-    assert (small["block_m"], small["waves"]) == (128, 4)
+    assert (small["block_m"], small["waves"]) == (128, 8)
+    # ... unless the keys are too few to share (under 4 key tiles)
+    short = fa.fa_query_config(fa.FA_F16, 128, 0, 2, 8, 1024, 192)
+    assert (short["block_m"], short["waves"]) == (128, 4)
+    # between the two: the plain 4-wave kernel
+    mid = fa.fa_query_config(fa.FA_BF16, 128, 1, 1, 64, 777, 777)
+    assert (mid["block_m"], mid["waves"]) == (128, 4)
+    # d = 256 never splits its keys (the merge buffer would not fit)
+    wide = fa.fa_query_config(fa.FA_BF16, 256, 0, 1, 2, 1024, 1024)
+    assert (wide["block_m"], wide["waves"]) == (128, 4)
 
 
 def test_query_config_rejects_bad_sizes():

@@ -256,15 +256,17 @@ def test_one_hot_wide_score_range(dt, d, sk, gpu):
     assert float(np.abs(lse[0, 0].double().cpu().numpy() - (64.0 + np.log(cnt))).max()) <= TOL_LSE
 
 
-@pytest.mark.parametrize("b,h,sq,waves", [(2, 4, 777, 4), (1, 256, 4096, 8), (1, 300, 1000, 8)])
-def test_deterministic(b, h, sq, waves, gpu):
-    """Two runs give the same bits, for the 4-wave kernel and for the 8-wave
-    ping-pong kernel (which has no barrier between the two slots of a key
-    window, so a race on an LDS stage would show up as run-to-run noise), on
-    its per-item and on its persistent grid."""
+@pytest.mark.parametrize("b,h,sq,waves,block_m", [(1, 64, 777, 4, 128), (2, 4, 777, 8, 128), (1, 256, 4096, 8, 256),
+                                                 (1, 300, 1000, 8, 256)])
+def test_deterministic(b, h, sq, waves, block_m, gpu):
+    """Two runs give the same bits, for the 4-wave kernel, for it with two key
+    groups (merged in a fixed order), and for the 8-wave ping-pong kernel
+    (which has no barrier between the two slots of a key window, so a race on
+    an LDS stage would show up as run-to-run noise), on its per-item and on its
+    persistent grid."""
     import torch
     cfg = fa.fa_query_config(W.DTYPE_CODE["bf16"], 128, 1, b, h, sq, sq)
-    assert cfg["waves"] == waves
+    assert (cfg["waves"], cfg["block_m"]) == (waves, block_m)
     w = W.shape("det", "bf16", b, h, sq, sq, 128, True, seed=9)
     q, k, v = (t.cuda() for t in W.make(w))
     o1, l1 = fa.attention(q, k, v, causal=True)
@@ -287,7 +289,7 @@ def test_eight_waves_equal_four_waves(dt, h, sq, sk, causal, gpu):
     are held to the oracle's tolerance instead."""
     import torch
     cfg = fa.fa_query_config(W.DTYPE_CODE[dt], 128, int(causal), 1, h, sq, sk)
-    assert cfg["waves"] == 8
+    assert (cfg["waves"], cfg["block_m"]) == (8, 256)
     launch = fa.fa_query_launch(W.DTYPE_CODE[dt], 128, int(causal), 1, h, sq, sk)
     w = W.shape("waves", dt, 1, h, sq, sk, 128, causal, seed=sq + sk)
     q, k, v = (t.cuda() for t in W.make(w))

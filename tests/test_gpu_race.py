@@ -8,7 +8,7 @@ tolerance might let through.  Each case runs through the poisoned build and is
 compared with the fp64 oracle element by element, exactly as in the parity
 tests.  The shapes cover every kernel that copies into LDS: the 8-wave
 ping-pong forward (per-item and persistent grids, causal, ragged, sq != sk),
-the 4-wave forward (d = 64, 128, 256), split-KV, variable-length sequences,
+the 4-wave forward (d = 64, 128, 256) and its two-key-group form, split-KV, variable-length sequences,
 the backward (dense and variable-length) and the FP8 forward.  The number of waves per workgroup is varied
 by the shapes themselves (4 and 8 waves run the same tiles), and
 test_gpu_parity compares the two bit for bit on shared rows.
@@ -33,8 +33,9 @@ FWD = [
     ("bf16", 1, 256, 300, 520, 128, False, 8, False),
     ("f16", 1, 256, 1000, 333, 128, True, 8, False),
     ("bf16", 1, 320, 512, 512, 128, True, 8, True),
-    ("f16", 2, 8, 1024, 1024, 128, False, 4, False),
-    ("bf16", 1, 3, 333, 700, 64, True, 4, False),
+    ("f16", 2, 8, 1024, 1024, 128, False, 8, False),      # 4 waves x 2 key groups
+    ("bf16", 1, 3, 333, 700, 64, True, 8, False),         # 4 waves x 2 key groups
+    ("bf16", 1, 64, 777, 777, 128, True, 4, False),       # 4 waves
     ("bf16", 2, 2, 250, 250, 256, False, 4, False),
 ]
 
