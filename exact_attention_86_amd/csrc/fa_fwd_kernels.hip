@@ -855,13 +855,20 @@ fa_fwd_16pp(Params p)
         auto xphase = [&](int n0) {
             const bool need_mask = (n0 + BN > sk) || (CAUSAL && n0 + BN - 1 > wq_first);
             if (need_mask) {
+                // score r of block kb is key n0 + 32kb + 4g + off(r), alive iff
+                // key <= min(sk - 1, qrow) (causal) or sk - 1: the sign of the
+                // difference selects -inf (no per-element compare, whose lane
+                // masks would take scalar registers)
+                const int lim0 = (CAUSAL ? min(sk - 1, qrow) : sk - 1) - n0 - 4 * g;
 #pragma unroll
                 for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        const int key = n0 + kb * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
-                        const bool dead = (key >= sk) || (CAUSAL && key > qrow);
-                        if (dead) s[kb][r] = -INFINITY;
+                        const int off = kb * 32 + (r >> 2) * 8 + (r & 3);
+                        const uint32_t dead = (uint32_t)((lim0 - off) >> 31);
+                        const float x = s[kb][r];  // through a scalar: a bit cast of a vector element reads element 0
+                        const uint32_t bits = __builtin_bit_cast(uint32_t, x);
+                        s[kb][r] = __builtin_bit_cast(float, (bits & ~dead) | (0xff800000u & dead));
                     }
             }
             float lsum = 0.f;
