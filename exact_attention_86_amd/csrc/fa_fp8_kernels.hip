@@ -208,12 +208,16 @@ fa_fwd_fp8(Fp8Params p)
         // ---- masks (ragged keys, causal diagonal) on the raw scores, tile max ----
         const bool need_mask = (n0 + BN > sk) || (CAUSAL && n0 + BN - 1 > wq);
         if (need_mask) {
+            // score r of block kb is key n0 + 32kb + 4g + off(r); it lives iff
+            // key <= min(sk - 1, qrow) (causal) or sk - 1: one compare and one
+            // select per score against a bound folded once per tile
+            const int lim0 = (CAUSAL ? min(sk - 1, qrow) : sk - 1) - n0 - 4 * g;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int key = n0 + kb * 32 + (r >> 2) * 8 + 4 * g + (r & 3);
-                    if (key >= sk || (CAUSAL && key > qrow)) s[kb][r] = -INFINITY;
+                    const int off = kb * 32 + (r >> 2) * 8 + (r & 3);
+                    s[kb][r] = off <= lim0 ? s[kb][r] : -INFINITY;
                 }
         }
         float mx = s[0][0];
