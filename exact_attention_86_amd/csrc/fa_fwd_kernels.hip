@@ -632,8 +632,8 @@ fa_fwd_16(Params p)
 // VALU work.  The slots need no barrier between them (no LDS stage changes
 // hands inside a window), so a wave moves on as soon as its own phase ends.
 // K(t) and V(t-1) are read inside window t; the copies of K(t+1) and V(t) go
-// out at its start into the stages freed by window t-1 and are awaited before
-// the barrier that ends it.  Group A's wave i owns query
+// out during it (each wave's at the start of its own softmax phase) into the
+// stages freed by window t-1 and are awaited before the barrier that ends it.  Group A's wave i owns query
 // rows [64i, 64i+32) of the 256-row tile and group B's wave i rows
 // [64i+32, 64i+64), so both groups reach the causal diagonal together.
 template <int D, int BN, bool BF16, bool CAUSAL, bool PERSIST>
@@ -947,19 +947,21 @@ fa_fwd_16pp(Params p)
         const int nslots = 2 * nkv + 2;
         for (int k = 0; k < nslots; k += 4) {
             const int t = k >> 1;
-            // slot k = 2t (t even): A: M(t), B: X(t-1); copies K(t+1), V(t)
-            issue(Stage<1>{}, Stage<0>{}, t);
-            if (grp == 0) do_m(Stage<0>{}, t); else do_x(t - 1);
+            // slot k = 2t (t even): A: M(t), B: X(t-1); copies K(t+1), V(t).
+            // Each wave issues its copies at the start of its own softmax
+            // phase, so their issue overlaps the partner wave's matrix-core
+            // phase instead of delaying it (the stages they fill were last
+            // read before the barrier that opened this window)
+            if (grp == 0) do_m(Stage<0>{}, t); else { issue(Stage<1>{}, Stage<0>{}, t); do_x(t - 1); }
             // slot 2t+1: A: X(t), B: M(t)
-            if (grp == 0) do_x(t); else do_m(Stage<0>{}, t);
+            if (grp == 0) { issue(Stage<1>{}, Stage<0>{}, t); do_x(t); } else do_m(Stage<0>{}, t);
             wait_copies();
             lds_barrier();
             if (k + 2 >= nslots) break;
             // slot 2t+2 = 2(t+1) (t+1 odd): A: M(t+1), B: X(t); copies K(t+2), V(t+1)
-            issue(Stage<0>{}, Stage<1>{}, t + 1);
-            if (grp == 0) do_m(Stage<1>{}, t + 1); else do_x(t);
+            if (grp == 0) do_m(Stage<1>{}, t + 1); else { issue(Stage<0>{}, Stage<1>{}, t + 1); do_x(t); }
             // slot 2t+3: A: X(t+1), B: M(t+1)
-            if (grp == 0) do_x(t + 1); else do_m(Stage<1>{}, t + 1);
+            if (grp == 0) { issue(Stage<0>{}, Stage<1>{}, t + 1); do_x(t + 1); } else do_m(Stage<1>{}, t + 1);
             wait_copies();
             lds_barrier();
         }
