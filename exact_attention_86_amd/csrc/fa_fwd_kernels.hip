@@ -275,7 +275,13 @@ fa_fwd_16(Params p)
     };
     // copies of the next tile are spread over the current tile's matrix-core
     // work (K copies after each 32-key score block, V copies after each
-    // 16-key PV chunk) instead of one burst that stalls the wave at issue
+    // 16-key PV chunk) instead of one burst that stalls the wave at issue.
+    // Non-causal d = 256 (32-key tiles, one score block) takes them in one
+    // burst between the score products and the softmax instead: measured 4.6 %
+    // faster there; the same change made the causal d = 256 variant 68 %
+    // slower (the compiler moved its register spills into the loop) and d = 128
+    // with two key groups 3 % slower, so those keep the spread copies.
+    constexpr bool COPY_BURST = D > 128 && !CAUSAL;
     constexpr int KC_PER = (DMA + NKB - 1) / NKB;
     constexpr int VC_PER = (DMA + 2 * NKB - 1) / (2 * NKB);
 
@@ -361,12 +367,17 @@ fa_fwd_16(Params p)
 #pragma unroll
                     for (int qb = 0; qb < QB; ++qb) s[qb][kb] = mfma16(a, qf[qb][kk], s[qb][kb], BF16);
                 }
-                if (PF_FULL)
+                if (PF_FULL && !COPY_BURST)
                     static_for<DMA>([&](auto j) {
                         if (j.value >= kb * KC_PER && j.value < (kb + 1) * KC_PER)
                             copy_k(j, Stage<S ^ 1>{}, nn, true);
                     });
             }
+            if (PF_FULL && COPY_BURST)
+                static_for<DMA>([&](auto j) {
+                    copy_k(j, Stage<S ^ 1>{}, nn, true);
+                    copy_v(j, Stage<S ^ 1>{}, nn, true);
+                });
 
             // ---- masks: ragged key tail, causal diagonal.  Score r of block kb
             //      is key n0 + 32kb + 4g + off(r); it lives iff key <= lim =
@@ -477,7 +488,7 @@ fa_fwd_16(Params p)
 #pragma unroll
                     for (int qb = 0; qb < QB; ++qb) oacc[qb][dt] = mfma16(a, pk[qb][kc], oacc[qb][dt], BF16);
                 }
-                if (PF_FULL)
+                if (PF_FULL && !COPY_BURST)
                     static_for<DMA>([&](auto j) {
                         if (j.value >= kc * VC_PER && j.value < (kc + 1) * VC_PER)
                             copy_v(j, Stage<S ^ 1>{}, nn, true);
