@@ -28,6 +28,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import math
 import os
@@ -101,12 +102,28 @@ def shader_clock(torch_mod, fa_mod, step, stream, n: int = 24, ticks: int = 2000
                       "%d us) right behind each of %d launches after the timed region" % (ticks // 100, n)}
 
 
-def kernel_sha() -> str:
+# C/C++ string and character literals (kept) or comments (dropped)
+_LITERAL_OR_COMMENT = re.compile(r'"(?:\\.|[^"\\\n])*"|\'(?:\\.|[^\'\\\n])*\'|//[^\n]*|/\*.*?\*/', re.S)
+
+
+def source_digest(texts) -> str:
+    """sha256[:16] of C/C++ sources with comments removed and whitespace
+    collapsed, so that edits to comments or layout do not mark a counter
+    record as taken on other code."""
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
-            h.update(f.read())
+    for t in texts:
+        code = _LITERAL_OR_COMMENT.sub(lambda m: " " if m.group(0)[0] == "/" else m.group(0), t)
+        h.update(" ".join(code.split()).encode())
+        h.update(b"\0")
     return h.hexdigest()[:16]
+
+
+def kernel_sha() -> str:
+    texts = []
+    for p in KERNEL_SOURCES:
+        with open(p, encoding="utf-8") as f:
+            texts.append(f.read())
+    return source_digest(texts)
 
 
 def traffic_record(w: W.Workload):

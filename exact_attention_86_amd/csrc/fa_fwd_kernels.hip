@@ -191,7 +191,8 @@ fa_fwd_16(Params p)
     if (!map_item(p, bh, item)) return;
 
     const int tid = threadIdx.x;
-    // (both wave-uniform; said so, so that every branch on them is uniform)
+    // (both wave-uniform; readfirstlane tells the compiler so, which keeps the
+    // branches on them uniform and the copy bases in scalar registers)
     const int kg = KG > 1 ? __builtin_amdgcn_readfirstlane((tid >> 6) / NW) : 0;  // key group
     const int w = KG > 1 ? __builtin_amdgcn_readfirstlane((tid >> 6) % NW) : tid >> 6;  // wave within it
     const int lane = tid & 63;
@@ -644,9 +645,10 @@ fa_fwd_16(Params p)
 // hands inside a window), so a wave moves on as soon as its own phase ends.
 // K(t) and V(t-1) are read inside window t; the copies of K(t+1) and V(t) go
 // out during it (each wave's at the start of its own softmax phase) into the
-// stages freed by window t-1 and are awaited before the barrier that ends it.  Group A's wave i owns query
-// rows [64i, 64i+32) of the 256-row tile and group B's wave i rows
-// [64i+32, 64i+64), so both groups reach the causal diagonal together.
+// stages freed by window t-1 and are awaited before the barrier that ends it.
+// Group A's wave i owns query rows [64i, 64i+32) of the 256-row tile and
+// group B's wave i rows [64i+32, 64i+64), so both groups reach the causal
+// diagonal together.
 template <int D, int BN, bool BF16, bool CAUSAL, bool PERSIST>
 __global__ void __launch_bounds__(512, 1)
 fa_fwd_16pp(Params p)

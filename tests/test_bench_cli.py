@@ -55,6 +55,19 @@ def test_stale_traffic_record_is_dropped(monkeypatch):
     assert bench.traffic_record(w) is None
 
 
+def test_source_digest_ignores_comments_and_layout_only():
+    sys.path.insert(0, ROOT)
+    import bench
+    a = 'int f() { // note\n  return 1; /* block\n comment */ }\nconst char* s = "x // y";\n'
+    same = 'int f() {\n    return 1;   }\nconst char* s = "x // y";   // trailing\n'
+    code = 'int f() { return 2; }\nconst char* s = "x // y";\n'
+    literal = 'int f() { return 1; }\nconst char* s = "x // z";\n'
+    assert bench.source_digest([a]) == bench.source_digest([same])
+    assert bench.source_digest([a]) != bench.source_digest([code])
+    assert bench.source_digest([a]) != bench.source_digest([literal])
+    assert len(bench.kernel_sha()) == 16
+
+
 def test_metric_names_the_workload_that_ran():
     sys.path.insert(0, ROOT)
     import argparse
