@@ -392,7 +392,13 @@ FA_API int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, f
     p.total_q = (int)total_q;
     p.total_k = (int)total_k;
 
-    hipError_t e = fa::launch_fwd_varlen(dtype, (int)d, p, (hipStream_t)stream);
+    // fewer tiles with rows than CUs (at most ceil(total_q / block_m) + batch
+    // per head; the grid's other items return at once) and at least 4 key
+    // tiles per sequence on average: two key groups per tile (8 waves), as
+    // fa_fwd does
+    const int64_t live_items = h * ((total_q + tc.block_m - 1) / tc.block_m + batch);
+    const bool kg = d <= 128 && live_items < 256 && total_k >= 4 * (int64_t)tc.block_n * batch;
+    hipError_t e = fa::launch_fwd_varlen(dtype, (int)d, p, kg, (hipStream_t)stream);
     if (e != hipSuccess) {
         snprintf(g_err, sizeof g_err, "fa_fwd_varlen: launch failed: %s", hipGetErrorString(e));
         return FA_ERR_HIP;

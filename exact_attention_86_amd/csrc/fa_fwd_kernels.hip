@@ -180,7 +180,7 @@ fa_fwd_16(Params p)
     static_assert(CPR >= 8, "swizzles need at least 8 chunks per row");
     static_assert(DMA >= 1 && NCH % (64 * NW) == 0, "tile must split evenly over waves");
     static_assert(KG * 2 * 2 * TB <= 160 * 1024, "LDS budget");
-    static_assert(KG == 1 || (KG == 2 && QB == 1 && !SPLIT && !VARLEN), "key groups: plain one-block tiles only");
+    static_assert(KG == 1 || (KG == 2 && QB == 1 && !SPLIT), "key groups: one-block tiles, not split-KV");
     constexpr int GROUP_BYTES = 2 * 2 * TB;  // one key group's two stages
 
     // [key group][stage][0 = K, 1 = V][BN rows x D], rows row-major with
@@ -1323,10 +1323,16 @@ static hipError_t launch16kg(const Params& p, hipStream_t s)
     return launch(fa_fwd_16<D, BN, 4, 1, BF16, false, false, false, 2>, 8, p, s);
 }
 
-// variable-length sequences (4-wave kernel)
+// variable-length sequences (4-wave kernel; with two key groups: 8 waves)
 template <int D, int BN, bool BF16>
-static hipError_t launch16varlen(const Params& p, hipStream_t s)
+static hipError_t launch16varlen(const Params& p, bool kg, hipStream_t s)
 {
+    if constexpr (D <= 128) {
+        if (kg) {
+            if (p.causal) return launch(fa_fwd_16<D, BN, 4, 1, BF16, true, false, true, 2>, 8, p, s);
+            return launch(fa_fwd_16<D, BN, 4, 1, BF16, false, false, true, 2>, 8, p, s);
+        }
+    }
     if (p.causal) return launch(fa_fwd_16<D, BN, 4, 1, BF16, true, false, true>, 4, p, s);
     return launch(fa_fwd_16<D, BN, 4, 1, BF16, false, false, true>, 4, p, s);
 }
@@ -1450,18 +1456,18 @@ hipError_t launch_fwd_split(int dtype, int d, const TileConfig& tc, const Params
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_fwd_varlen(int dtype, int d, const Params& p, hipStream_t s)
+hipError_t launch_fwd_varlen(int dtype, int d, const Params& p, bool kg, hipStream_t s)
 {
     switch (dtype) {
     case 2:
-        if (d == 64) return launch16varlen<64, 128, true>(p, s);
-        if (d == 128) return launch16varlen<128, 64, true>(p, s);
-        if (d == 256) return launch16varlen<256, 32, true>(p, s);
+        if (d == 64) return launch16varlen<64, 128, true>(p, kg, s);
+        if (d == 128) return launch16varlen<128, 64, true>(p, kg, s);
+        if (d == 256) return launch16varlen<256, 32, true>(p, false, s);
         break;
     case 1:
-        if (d == 64) return launch16varlen<64, 128, false>(p, s);
-        if (d == 128) return launch16varlen<128, 64, false>(p, s);
-        if (d == 256) return launch16varlen<256, 32, false>(p, s);
+        if (d == 64) return launch16varlen<64, 128, false>(p, kg, s);
+        if (d == 128) return launch16varlen<128, 64, false>(p, kg, s);
+        if (d == 256) return launch16varlen<256, 32, false>(p, false, s);
         break;
     }
     return hipErrorInvalidValue;

@@ -88,7 +88,7 @@ struct Fp8Params {
 bool tile_config(int dtype, int d, int64_t bh, int64_t sq, int64_t sk, int causal, TileConfig* tc);
 hipError_t launch_fwd(int dtype, int d, const TileConfig& tc, const Params& p, hipStream_t stream);
 bool tile_config_split(int dtype, int d, TileConfig* tc);
-hipError_t launch_fwd_varlen(int dtype, int d, const Params& p, hipStream_t stream);
+hipError_t launch_fwd_varlen(int dtype, int d, const Params& p, bool key_groups, hipStream_t stream);
 hipError_t launch_fwd_fp8(const Fp8Params& p, hipStream_t stream);
 bool bwd_supported(int dtype, int d);
 hipError_t launch_bwd(int dtype, int d, const BwdParams& p, hipStream_t stream);

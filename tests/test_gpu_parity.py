@@ -381,6 +381,9 @@ VARLEN = [
     ("bf16", 2, 128, True, [130, 257, 64], [130, 300, 64]),
     ("f16", 3, 64, True, [5, 0, 200], [7, 9, 150]),
     ("f16", 1, 256, False, [33, 129], [300, 1]),
+    # long keys, few tiles: two key groups per tile (8 waves)
+    ("bf16", 2, 128, True, [700, 1, 1500], [900, 300, 1500]),
+    ("f16", 2, 64, False, [333, 1000], [1200, 2000]),
 ]
 
 

@@ -61,6 +61,7 @@ def test_poisoned_split_kv(gpu):
 def test_poisoned_varlen(gpu):
     with fa.poisoned():
         P.test_varlen_per_sequence_compare(("bf16", 2, 128, True, (300, 17, 130), (300, 40, 129)), gpu)
+        P.test_varlen_per_sequence_compare(("bf16", 2, 128, True, (700, 1, 1500), (900, 300, 1500)), gpu)
 
 
 def test_poisoned_backward(gpu):
