@@ -1,7 +1,7 @@
 """Throughput of the exact-attention prefill forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--split N | --bwd | --fp8] [--no-cpu-baseline]
+                    [--split N | --bwd | --fp8 | --varlen N] [--no-cpu-baseline]
 
 One step is one fa_fwd call (the whole hot path: tile schedule, Q/K/V tile
 loads, S = QK^T, masking, online softmax, O += PV, epilogue) over the
@@ -12,6 +12,10 @@ is one fa_bwd call (the D = dO.O pass, the dK/dV kernel and the dQ kernel)
 on O and LSE that one fa_fwd call produced before timing; its FLOP count is
 the usual 2.5x the forward's (five sq x sk x d products where the forward has
 two), and the roofline covers the three kernels of the call together.
+With --varlen N a step is one fa_fwd_varlen call over N packed sequences of
+the workload's head count, head size, dtype and mask, with lengths uniform on
+[256, sq] (seeded; queries and keys alike); FLOP and bytes are summed per
+sequence with the same conventions.
 With --fp8 a step is one fa_fwd_fp8 call on the workload's draws quantized to
 OCP E4M3 with per-tensor power-of-two descale factors; its roofline is priced
 against the dense FP8 matrix peak and its oracle leg runs on the dequantized
@@ -56,6 +60,9 @@ KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_86_amd", "csrc", f)
 def metric_name(w: W.Workload, args) -> str:
     """The headline metric strings for the headline workload; otherwise the
     same form naming the workload that ran."""
+    if getattr(args, "varlen", 0):
+        return "attn fwd TFLOP/s, packed variable-length %s h%d d%d %s, %d sequences of %d-%d; %% of MFMA peak" % (
+            w.dtype, w.h, w.d, "causal" if w.causal else "non-causal", args.varlen, min(256, w.sq), w.sq)
     if w.name == W.HEADLINE.name:
         return METRIC_BWD if args.bwd else (METRIC_FP8 if args.fp8 else METRIC)
     kind = "bwd" if args.bwd else "fwd"
@@ -167,6 +174,35 @@ def cpu_baseline(w: W.Workload, q, k, v, budget_s: float):
                 nheads, w.b * w.h, w.sq, w.sk, dt)}
 
 
+def cpu_baseline_varlen(w: W.Workload, lens, q, k, v, budget_s: float):
+    """Time the fp64 oracle on whole sequences (all heads) of the packed batch
+    q, k, v [1, h, total, d], in order, about budget_s of CPU work, and scale
+    to TFLOP/s with the per-sequence FLOP convention."""
+    import oracle
+    nthreads = oracle.default_threads()
+    scale = float(np.float32(w.scale))
+    offs = np.concatenate([[0], np.cumsum(lens)]).astype(int)
+    seq_flops = [4.0 * w.h * n * n * w.d / (2 if w.causal else 1) for n in lens]
+    sl = lambda t, i, hs: t[:, hs, offs[i]:offs[i + 1]]
+    t0 = time.perf_counter()
+    oracle.attn(sl(q, 0, slice(0, 1)), sl(k, 0, slice(0, 1)), sl(v, 0, slice(0, 1)), scale, w.causal,
+                nthreads=nthreads)
+    rate = seq_flops[0] / w.h / max(time.perf_counter() - t0, 1e-4)
+    nseq, planned = 0, 0.0
+    while nseq < len(lens) and (nseq == 0 or planned + seq_flops[nseq] <= rate * budget_s):
+        planned += seq_flops[nseq]
+        nseq += 1
+    t0 = time.perf_counter()
+    for i in range(nseq):
+        oracle.attn(sl(q, i, slice(None)), sl(k, i, slice(None)), sl(v, i, slice(None)), scale, w.causal,
+                    nthreads=nthreads)
+    dt = time.perf_counter() - t0
+    return {"value": planned / dt / 1e12, "unit": "TFLOP/s", "cores": nthreads,
+            "cpu_model": cpu_model(), "kind": "oracle",
+            "sample": "the first %d of %d sequences (all %d heads, lengths %s), fp64 C oracle, %.1f s" % (
+                nseq, len(lens), w.h, ",".join(map(str, lens[:nseq])), dt)}
+
+
 def cpu_baseline_bwd(w: W.Workload, q, k, v, budget_s: float):
     """Time the oracle's backward on whole heads (about budget_s of CPU work;
     the oracle threads over heads, so at least one head per thread) and scale
@@ -206,6 +242,8 @@ def main():
                     help="time the backward (fa_bwd) instead of the forward")
     ap.add_argument("--fp8", action="store_true",
                     help="time the FP8 forward (fa_fwd_fp8) on E4M3-quantized inputs")
+    ap.add_argument("--varlen", type=int, default=0, metavar="N",
+                    help="time fa_fwd_varlen on N packed sequences with lengths uniform on [256, sq]")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -236,6 +274,15 @@ def main():
     if args.fp8 and (args.bwd or args.split > 1 or w.dtype == "f32"):
         print("--fp8 runs the forward of a 16-bit workload only", file=sys.stderr)
         sys.exit(2)
+    if args.varlen and (args.bwd or args.fp8 or args.split > 1 or w.dtype == "f32" or args.varlen < 1):
+        print("--varlen N (N >= 1) runs the 16-bit forward only", file=sys.stderr)
+        sys.exit(2)
+    lens = None
+    if args.varlen:
+        lens = W.varlen_lengths(args.varlen, min(256, w.sq), w.sq, w.seed)
+        total = sum(lens)
+        packed = W.shape("%s_varlen%d_total%d" % (w.name, args.varlen, total), w.dtype, 1, w.h, total,
+                         total, w.d, w.causal, scale=w.scale, seed=w.seed, qk_mult=w.qk_mult, v_dist=w.v_dist)
 
     import torch
     import exact_attention_86_amd as fa
@@ -252,17 +299,25 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_per_launch": n, "launches": args.steps}), flush=True)
         return
-    log("[bench] generating %s" % w.name)
-    q, k, v = W.make(w)
+    log("[bench] generating %s" % (packed.name if lens else w.name))
+    q, k, v = W.make(packed if lens else w)
     qd, kd, vd = (t.to(dev) for t in (q, k, v))
     od = torch.empty_like(qd)
+    flops = w.flops * (2.5 if args.bwd else 1.0)
+    alg_bytes = w.algorithmic_bytes
+    if lens:
+        # per-sequence conventions: 4 h L^2 d FLOP (halved when causal);
+        # Q, K, V, O once and the fp32 LSE
+        flops = sum(4.0 * w.h * n * n * w.d for n in lens) / (2 if w.causal else 1)
+        alg_bytes = packed.algorithmic_bytes
+        cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device=dev)
     if args.fp8:
         q8, k8, v8, desc = W.make_fp8(w)
         # the oracle leg sees the dequantized values the kernel computes on
         q, k, v = (t.to(torch.float64).numpy() * s for t, s in zip((q8, k8, v8), desc))
         qd, kd, vd = (t.to(dev) for t in (q8, k8, v8))
         od = torch.empty((w.b, w.h, w.sq, w.d), dtype=torch.bfloat16, device=dev)
-    lsed = torch.empty((w.b, w.h, w.sq), dtype=torch.float32, device=dev)
+    lsed = torch.empty(tuple(q.shape[:3]), dtype=torch.float32, device=dev)
     scale = float(np.float32(w.scale))
     stream = torch.cuda.current_stream(dev)
     code = W.DTYPE_CODE[w.dtype]
@@ -291,6 +346,15 @@ def main():
         def step():
             rc = fa.fa_fwd_split(*ptrs, w.b, w.h, w.sq, w.sk, w.d, scale, int(w.causal), code,
                                  args.split, ws.data_ptr(), ws_bytes, stream.cuda_stream)
+            if rc != fa.FA_OK:
+                raise fa.FaError(rc, fa.fa_last_error())
+    elif lens:
+        vptrs = (qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), od.data_ptr(), lsed.data_ptr(),
+                 cu.data_ptr(), cu.data_ptr())
+
+        def step():
+            rc = fa.fa_fwd_varlen(*vptrs, len(lens), w.h, total, total, max(lens), w.d, scale,
+                                  int(w.causal), code, stream.cuda_stream)
             if rc != fa.FA_OK:
                 raise fa.FaError(rc, fa.fa_last_error())
     elif args.fp8:
@@ -333,7 +397,6 @@ def main():
     med_ms = sorted(per)[len(per) // 2]
     ms_per_step = wall * 1e3 / args.steps
 
-    flops = w.flops * (2.5 if args.bwd else 1.0)
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (avg_ms * 1e-3) / 1e12
     dtype = "fp8_e4m3" if args.fp8 else w.dtype
@@ -341,15 +404,20 @@ def main():
     log("[bench] shader clock: %s" % sclk)
     log("[bench] %s: wall %.3f ms/step, kernel avg %.3f ms (min %.3f, max %.3f), "
         "%.1f TFLOP/s = %.1f%% of %.1f; %.0f GB/s algorithmic" % (
-            w.name, ms_per_step, avg_ms, min(per), max(per), achieved,
-            100 * achieved / peak, peak, w.algorithmic_bytes / (avg_ms * 1e-3) / 1e9))
+            packed.name if lens else w.name, ms_per_step, avg_ms, min(per), max(per), achieved,
+            100 * achieved / peak, peak, alg_bytes / (avg_ms * 1e-3) / 1e9))
 
     # the matrix peak scales with the shader clock: % of peak at the clock seen
     frac_sclk = None
     if sclk.get("mhz_median"):
         frac_sclk = round(achieved / (peak * sclk["mhz_median"] / 2400.0), 4)
-    kernel = "fa_bwd" if args.bwd else ("fa_fwd_fp8" if args.fp8 else
-                                         ("fa_fwd" if args.split == 1 else "fa_fwd_split"))
+    kernel = "fa_bwd" if args.bwd else ("fa_fwd_fp8" if args.fp8 else ("fa_fwd_varlen" if lens else
+                                         ("fa_fwd" if args.split == 1 else "fa_fwd_split")))
+    config = dict(w.describe(), kernel=kernel, nsplit=args.split, parallelism="none (one GPU)")
+    if lens:
+        config.update(workload=packed.name, b=1, sq=total, sk=total, seq_lens=lens,
+                      lens_recipe="uniform integers on [%d, %d], numpy default_rng(%d)" % (
+                          min(256, w.sq), w.sq, w.seed))
     out = {
         "metric": metric_name(w, args),
         "value": round(value, 3),
@@ -363,7 +431,7 @@ def main():
         "vs_baseline": None,
         "dtype": dtype,
         "data": "synthetic",
-        "config": dict(w.describe(), kernel=kernel, nsplit=args.split, parallelism="none (one GPU)"),
+        "config": config,
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": traffic_record(w) if kernel == "fa_fwd" else None},
@@ -371,8 +439,8 @@ def main():
                       "min": round(min(per) * 1e3, 2), "max": round(max(per) * 1e3, 2),
                       "calls": args.steps, "timed_ms": round(sum(per), 1)},
         "tflops_at_median": round(flops / (med_ms * 1e-3) / 1e12, 3),
-        "gbps_algorithmic": round(w.algorithmic_bytes / (avg_ms * 1e-3) / 1e9, 1),
-        "hbm_frac_algorithmic": round(w.algorithmic_bytes / (avg_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "gbps_algorithmic": round(alg_bytes / (avg_ms * 1e-3) / 1e9, 1),
+        "hbm_frac_algorithmic": round(alg_bytes / (avg_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         "sclk": sclk,
         "peak_at_sclk": None if frac_sclk is None else round(peak * sclk["mhz_median"] / 2400.0, 1),
         "frac_at_sclk": frac_sclk,
@@ -381,6 +449,8 @@ def main():
         log("[bench] timing the oracle on a sample (~%.0f s)" % args.cpu_budget)
         if args.bwd:
             out["cpu_baseline"] = cpu_baseline_bwd(w, q, k, v, args.cpu_budget)
+        elif lens:
+            out["cpu_baseline"] = cpu_baseline_varlen(w, lens, q, k, v, args.cpu_budget)
         else:
             out["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_budget)
     else:

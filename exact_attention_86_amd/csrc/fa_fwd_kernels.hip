@@ -649,10 +649,20 @@ fa_fwd_16(Params p)
 // Group A's wave i owns query rows [64i, 64i+32) of the 256-row tile and
 // group B's wave i rows [64i+32, 64i+64), so both groups reach the causal
 // diagonal together.
-template <int D, int BN, bool BF16, bool CAUSAL, bool PERSIST>
+// VARLEN: packed variable-length sequences (at most 64); a work item is one
+// causal pair (or, without the mask, one query tile) of one sequence of one
+// head, and every address is offset to that sequence.  Items run in cost
+// order with the heads innermost: workgroup t takes head t mod h of the
+// (t / h)-th item, counting the sequences' items in descending order of
+// the sequence's cost (causal: its query tiles; else its keys; ties by
+// index).  The heaviest items start first, and with h a multiple of 8 every
+// item of a head runs on one XCD (workgroup t is dispatched to XCD t mod 8),
+// whose L2 then serves that head's K/V to all of them.
+template <int D, int BN, bool BF16, bool CAUSAL, bool PERSIST, bool VARLEN = false>
 __global__ void __launch_bounds__(512, 1)
 fa_fwd_16pp(Params p)
 {
+    static_assert(!(PERSIST && VARLEN), "the persistent schedule walks dense heads only");
     constexpr int NW = 8;                // waves per workgroup
     constexpr int BM = 256;              // query rows per workgroup tile
     constexpr int NKB = BN / 32;         // 32-key blocks per key tile
@@ -673,7 +683,7 @@ fa_fwd_16pp(Params p)
     __shared__ __attribute__((aligned(16))) uint16_t lds[4][TILE];
 
     int bh = 0, item = 0;
-    if constexpr (!PERSIST) {
+    if constexpr (!PERSIST && !VARLEN) {
         if (!map_item(p, bh, item)) return;
     }
 
@@ -684,7 +694,7 @@ fa_fwd_16pp(Params p)
     const int lane = tid & 63;
     const int l32 = lane & 31;
     const int g = lane >> 5;
-    const int sq = p.sq, sk = p.sk;
+    int sq = p.sq, sk = p.sk;  // per sequence when VARLEN
     const float c = p.c;  // |scale| * log2(e)
     constexpr float kRescaleThreshold = 8.f;
     constexpr float kRescaleLimit = 256.f;
@@ -694,11 +704,13 @@ fa_fwd_16pp(Params p)
     const uint16_t* __restrict__ K = nullptr;
     const uint16_t* __restrict__ V = nullptr;
     uint16_t* __restrict__ O = nullptr;
+    size_t lse0 = 0;  // LSE index of the slice's first row
     auto set_head = [&](int h) {
         Q = (const uint16_t*)p.q + (size_t)h * sq * D;
         K = (const uint16_t*)p.k + (size_t)h * sk * D;
         V = (const uint16_t*)p.v + (size_t)h * sk * D;
         O = (uint16_t*)p.o + (size_t)h * sq * D;
+        lse0 = (size_t)h * sq;
     };
 
     // ---- copies: wave w fills LDS chunks (w*DMA + j)*64 + lane of a tile ----
@@ -713,7 +725,8 @@ fa_fwd_16pp(Params p)
     const uint32_t lbase = __builtin_amdgcn_readfirstlane(lds_addr(&lds[0][0]) + w * DMA * 1024);
     auto copy_k = [&](auto j_tag, auto st_tag, int n0, bool full) {
         constexpr int J = decltype(j_tag)::value, ST = decltype(st_tag)::value;
-        const uint16_t* src = K + (size_t)n0 * D;
+        const void* src = K + (size_t)n0 * D;
+        if constexpr (VARLEN) src = uniform_ptr(src);
         if (full) {
             copy_1k<ST * TB + J * 1024>(src, dk[J], lbase);
         } else {
@@ -724,7 +737,8 @@ fa_fwd_16pp(Params p)
     };
     auto copy_v = [&](auto j_tag, auto st_tag, int n0, bool full) {
         constexpr int J = decltype(j_tag)::value, ST = decltype(st_tag)::value;
-        const uint16_t* src = V + (size_t)n0 * D;
+        const void* src = V + (size_t)n0 * D;
+        if constexpr (VARLEN) src = uniform_ptr(src);
         if (full) {
             copy_1k<(2 + ST) * TB + J * 1024>(src, dv[J], lbase);
         } else {
@@ -992,7 +1006,7 @@ fa_fwd_16pp(Params p)
                     const uint32_t w1 = pack2(oacc[dt][rb * 4 + 2] * inv, oacc[dt][rb * 4 + 3] * inv, BF16);
                     *(u32x2_t*)(orow + dt * 32 + rb * 8 + g * 4) = u32x2_t{w0, w1};
                 }
-            if (g == 0) p.lse[(size_t)bh * sq + qrow] = (m_run + __log2f(l_tot)) * kLn2;
+            if (g == 0) p.lse[lse0 + qrow] = (m_run + __log2f(l_tot)) * kLn2;
         }
     };
 
@@ -1013,9 +1027,52 @@ fa_fwd_16pp(Params p)
         // key block nQ - T at time T and they share it in L2, where walking
         // up they would read block 0 again one after another, long after the
         // first tiles read it
-        set_head(bh);
         int mts[2];
-        const int nt = item_tiles(p, item, mts);
+        int nt;
+        if constexpr (VARLEN) {
+            // lane i holds sequence i: its lengths (offsets clamped into
+            // [0, total], so malformed offsets cannot address outside the
+            // buffers), its item count and cost, and the number of items of
+            // the sequences ranked before it
+            int q0i = 0, k0i = 0, sqi = 0, ski = 0;
+            if (lane < p.batch) {
+                q0i = min(max(p.cu_q[lane], 0), p.total_q);
+                k0i = min(max(p.cu_k[lane], 0), p.total_k);
+                sqi = min(max(p.cu_q[lane + 1], q0i), p.total_q) - q0i;
+                ski = min(max(p.cu_k[lane + 1], k0i), p.total_k) - k0i;
+            }
+            const int nti = (sqi + BM - 1) / BM;
+            const int cnt = ski > 0 ? (CAUSAL ? (nti + 1) / 2 : nti) : 0;
+            const int cost = CAUSAL ? nti : ski;
+            int first = 0;
+            for (int jj = 0; jj < p.batch; ++jj) {
+                const int cj = __builtin_amdgcn_readlane(cost, jj);
+                const int nj = __builtin_amdgcn_readlane(cnt, jj);
+                first += (cj > cost || (cj == cost && jj < lane)) ? nj : 0;
+            }
+            const int t = blockIdx.x;
+            const int r = t / p.bh;
+            bh = t - r * p.bh;
+            const uint64_t mine = __builtin_amdgcn_ballot_w64(cnt > 0 && r >= first && r < first + cnt);
+            if (mine == 0) return;  // past the last item: the whole workgroup leaves
+            const int seq = __builtin_ffsll((long long)mine) - 1;
+            const int j = r - __builtin_amdgcn_readlane(first, seq);
+            const int q0s = __builtin_amdgcn_readlane(q0i, seq), k0s = __builtin_amdgcn_readlane(k0i, seq);
+            sq = __builtin_amdgcn_readlane(sqi, seq);
+            sk = __builtin_amdgcn_readlane(ski, seq);
+            const int ntiles = (sq + BM - 1) / BM;
+            Q = (const uint16_t*)p.q + ((size_t)bh * p.total_q + q0s) * D;
+            K = (const uint16_t*)p.k + ((size_t)bh * p.total_k + k0s) * D;
+            V = (const uint16_t*)p.v + ((size_t)bh * p.total_k + k0s) * D;
+            O = (uint16_t*)p.o + ((size_t)bh * p.total_q + q0s) * D;
+            lse0 = (size_t)bh * p.total_q + q0s;
+            mts[0] = CAUSAL ? ntiles - 1 - j : j;
+            mts[1] = j;
+            nt = (CAUSAL && mts[0] != mts[1]) ? 2 : 1;
+        } else {
+            set_head(bh);
+            nt = item_tiles(p, item, mts);
+        }
         process(Stage<0>{}, mts[0]);
         if (nt > 1) {
             __syncthreads();  // every wave is done with the LDS stages
@@ -1361,6 +1418,14 @@ static hipError_t launch16pp(const Params& p, bool persist, hipStream_t s)
     return launch(fa_fwd_16pp<D, BN, BF16, false, false>, 8, p, s);
 }
 
+// variable-length sequences on the ping-pong kernel
+template <int D, int BN, bool BF16>
+static hipError_t launch16ppvarlen(const Params& p, hipStream_t s)
+{
+    if (p.causal) return launch(fa_fwd_16pp<D, BN, BF16, true, false, true>, 8, p, s);
+    return launch(fa_fwd_16pp<D, BN, BF16, false, false, true>, 8, p, s);
+}
+
 template <int D, int BN, int NW>
 static hipError_t launch32(const Params& p, hipStream_t s)
 {
@@ -1456,17 +1521,24 @@ hipError_t launch_fwd_split(int dtype, int d, const TileConfig& tc, const Params
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_fwd_varlen(int dtype, int d, const Params& p, bool kg, hipStream_t s)
+hipError_t launch_fwd_varlen(int dtype, int d, const Params& p, int mode, hipStream_t s)
 {
+    const bool kg = mode == 1;
     switch (dtype) {
     case 2:
         if (d == 64) return launch16varlen<64, 128, true>(p, kg, s);
-        if (d == 128) return launch16varlen<128, 64, true>(p, kg, s);
+        if (d == 128) {
+            if (mode == 2) return launch16ppvarlen<128, 64, true>(p, s);
+            return launch16varlen<128, 64, true>(p, kg, s);
+        }
         if (d == 256) return launch16varlen<256, 32, true>(p, false, s);
         break;
     case 1:
         if (d == 64) return launch16varlen<64, 128, false>(p, kg, s);
-        if (d == 128) return launch16varlen<128, 64, false>(p, kg, s);
+        if (d == 128) {
+            if (mode == 2) return launch16ppvarlen<128, 64, false>(p, s);
+            return launch16varlen<128, 64, false>(p, kg, s);
+        }
         if (d == 256) return launch16varlen<256, 32, false>(p, false, s);
         break;
     }

@@ -30,6 +30,7 @@ struct Params {
     const int* cu_q;     // varlen: sequence offsets into the packed query rows (batch + 1)
     const int* cu_k;     // varlen: sequence offsets into the packed key rows (batch + 1)
     int total_q, total_k;  // varlen: packed rows per head
+    int batch;             // varlen: sequences
 };
 
 struct TileConfig {
@@ -88,7 +89,10 @@ struct Fp8Params {
 bool tile_config(int dtype, int d, int64_t bh, int64_t sq, int64_t sk, int causal, TileConfig* tc);
 hipError_t launch_fwd(int dtype, int d, const TileConfig& tc, const Params& p, hipStream_t stream);
 bool tile_config_split(int dtype, int d, TileConfig* tc);
-hipError_t launch_fwd_varlen(int dtype, int d, const Params& p, bool key_groups, hipStream_t stream);
+// mode 0: the 4-wave kernel; 1: with two key groups (d <= 128); 2: the
+// ping-pong kernel (d = 128, at most 64 sequences; the grid covers
+// h * batch * (items of the longest sequence), cost-ordered, the rest exit)
+hipError_t launch_fwd_varlen(int dtype, int d, const Params& p, int mode, hipStream_t stream);
 hipError_t launch_fwd_fp8(const Fp8Params& p, hipStream_t stream);
 bool bwd_supported(int dtype, int d);
 hipError_t launch_bwd(int dtype, int d, const BwdParams& p, hipStream_t stream);

@@ -27,7 +27,9 @@ def test_more_than_one_gpu_is_refused_with_a_message():
 @pytest.mark.parametrize("args", [["--bwd", "--split", "4"], ["--fp8", "--bwd"],
                                   ["--fp8", "--workload", "tiny_fp32_b1h2s128d64"],
                                   ["--shape", "bf16,1,2,3"], ["--shape", "q8,1,1,64,64,128,0"],
-                                  ["--shape", "bf16,1,1,64,64,128,2"]])
+                                  ["--shape", "bf16,1,1,64,64,128,2"], ["--varlen", "4", "--bwd"],
+                                  ["--varlen", "4", "--fp8"], ["--varlen", "4", "--split", "2"],
+                                  ["--varlen", "-1"], ["--varlen", "4", "--workload", "tiny_fp32_b1h2s128d64"]])
 def test_exclusive_options_are_refused_before_any_device_call(args):
     r = run_bench(*args)
     assert r.returncode == 2, r.stderr
@@ -78,3 +80,13 @@ def test_metric_names_the_workload_that_ran():
     assert bench.metric_name(W.HEADLINE, argparse.Namespace(bwd=False, fp8=True)) == bench.METRIC_FP8
     other = W.BY_NAME["prefill_fp16_b2h8s1024d128"]
     assert other.name in bench.metric_name(other, a)
+    v = bench.metric_name(W.HEADLINE, argparse.Namespace(bwd=False, fp8=False, varlen=16))
+    assert "variable-length" in v and "16 sequences of 256-4096" in v and v != bench.METRIC
+
+
+def test_varlen_lengths_are_seeded_and_in_range():
+    a = W.varlen_lengths(16, 256, 4096, 3)
+    assert a == W.varlen_lengths(16, 256, 4096, 3)
+    assert a != W.varlen_lengths(16, 256, 4096, 4)
+    assert len(a) == 16 and all(256 <= n <= 4096 for n in a)
+    assert W.varlen_lengths(50, 7, 7, 0) == [7] * 50

@@ -275,18 +275,33 @@ def test_deterministic(b, h, sq, waves, block_m, gpu):
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
+def four_wave_head_chunk(h, sq, sk, causal):
+    """Heads per fa_fwd_varlen call (a divisor of h) for which a one-sequence
+    call keeps the plain 4-wave kernel: fewer than 1024 rows or fewer than
+    256 ping-pong items (h * floor(sq / 256), halved when causal) and, unless
+    the keys span fewer than 4 tiles of 64, at least 256 row tiles
+    (h * (ceil(sq / 128) + 1)), so that neither the ping-pong kernel nor two
+    key groups are chosen."""
+    def plain(c):
+        pp = sq >= 1024 and c * (sq // 256) // (2 if causal else 1) >= 256
+        kg = c * (-(-sq // 128) + 1) < 256 and sk >= 4 * 64
+        return not pp and not kg
+    return max(c for c in range(1, h + 1) if h % c == 0 and plain(c))
+
+
 @pytest.mark.parametrize("dt,h,sq,sk,causal", [("bf16", 256, 4096, 4096, True), ("f16", 256, 333, 200, True),
                                               ("bf16", 300, 260, 390, False), ("bf16", 300, 1000, 1000, True)])
 def test_eight_waves_equal_four_waves(dt, h, sq, sk, causal, gpu):
     """The same problem through the 8-wave ping-pong kernel (fa_fwd on many
-    heads) and through the 4-wave kernel (fa_fwd_varlen with one sequence per
-    head set) gives the same bits: both run each 32-row query block through
-    the same instruction sequence per 64-key tile, in ascending key order, so
-    any difference means a stage was read before its copy landed or after it
-    was overwritten.  On the per-item causal grid the ping-pong kernel walks
-    the light tile of each pair (query tiles below nQ/2, 256 rows each) in
-    descending key order: those rows are the same sums in another order and
-    are held to the oracle's tolerance instead."""
+    heads) and through the 4-wave kernel (fa_fwd_varlen with one sequence, on
+    head chunks small enough to keep that kernel) gives the same bits: both
+    run each 32-row query block through the same instruction sequence per
+    64-key tile, in ascending key order, so any difference means a stage was
+    read before its copy landed or after it was overwritten.  On the per-item
+    causal grid the ping-pong kernel walks the light tile of each pair (query
+    tiles below nQ/2, 256 rows each) in descending key order: those rows are
+    the same sums in another order and are held to the oracle's tolerance
+    instead."""
     import torch
     cfg = fa.fa_query_config(W.DTYPE_CODE[dt], 128, int(causal), 1, h, sq, sk)
     assert (cfg["waves"], cfg["block_m"]) == (8, 256)
@@ -297,7 +312,13 @@ def test_eight_waves_equal_four_waves(dt, h, sq, sk, causal, gpu):
     o8, l8 = fa.attention(q, k, v, causal=causal, scale=s)
     cu_q = torch.tensor([0, sq], dtype=torch.int32, device="cuda")
     cu_k = torch.tensor([0, sk], dtype=torch.int32, device="cuda")
-    o4, l4 = fa.attention_varlen(q[0], k[0], v[0], cu_q, cu_k, sq, causal=causal, scale=s)
+    hc = four_wave_head_chunk(h, sq, sk, causal)
+    note(f"[eight-vs-four] {dt} h{h} sq{sq} sk{sk} causal={causal}: 4-wave on chunks of {hc} heads")
+    parts = [fa.attention_varlen(q[0, i:i + hc].contiguous(), k[0, i:i + hc].contiguous(),
+                                 v[0, i:i + hc].contiguous(), cu_q, cu_k, sq, causal=causal, scale=s)
+             for i in range(0, h, hc)]
+    o4 = torch.cat([x[0] for x in parts])
+    l4 = torch.cat([x[1] for x in parts])
     torch.cuda.synchronize()
     n_mt = -(-sq // cfg["block_m"])
     desc = min(sq, (n_mt // 2) * cfg["block_m"]) if causal and not launch["persistent"] else 0
@@ -384,11 +405,22 @@ VARLEN = [
     # long keys, few tiles: two key groups per tile (8 waves)
     ("bf16", 2, 128, True, [700, 1, 1500], [900, 300, 1500]),
     ("f16", 2, 64, False, [333, 1000], [1200, 2000]),
+    # d = 128, sequences of 1024 rows or more on average and a ping-pong work
+    # item per CU: the 8-wave ping-pong kernel, one item per (head, sequence,
+    # causal pair); sq > sk and sq < sk, a single row, a sequence shorter than
+    # one 256-row tile
+    ("bf16", 32, 128, True, [700, 1, 1500, 2048, 300, 4000], [900, 300, 1500, 2048, 300, 3000]),
+    ("f16", 16, 128, False, [1000, 2500, 1500, 129, 1, 1500], [1000, 2600, 1500, 1, 77, 1500]),
+    # 64 sequences: the ping-pong kernel's limit (one lane per sequence when it
+    # ranks them by cost); 65: the 4-wave kernel
+    ("bf16", 4, 128, False, [1000 + 13 * i for i in range(64)], [1000 + 13 * i for i in range(64)]),
+    ("f16", 4, 128, True, [1000 + 9 * i for i in range(65)], [1000 + 9 * i for i in range(65)]),
 ]
 
 
 @pytest.mark.parametrize("case", VARLEN, ids=lambda c: "%s-h%d-d%d-%s-%s" % (
-    c[0], c[1], c[2], "causal" if c[3] else "full", "_".join(map(str, c[4]))))
+    c[0], c[1], c[2], "causal" if c[3] else "full",
+    "_".join(map(str, c[4])) if len(c[4]) <= 8 else "%dseqs" % len(c[4])))
 def test_varlen_per_sequence_compare(case, gpu):
     import torch
     dt, h, d, causal, qlens, klens = case
@@ -420,3 +452,24 @@ def test_varlen_per_sequence_compare(case, gpu):
         el = float(np.max(np.abs(gl[:, q0:q1] - rl[0])))
         note(f"  seq {i}: sq={q1 - q0} sk={k1 - k0} O max-abs={eo:.3e} LSE max-abs={el:.3e}")
         assert eo <= TOL_O[dt] and el <= TOL_LSE
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_varlen_pingpong_equals_dense(causal, gpu):
+    """Equal-length sequences packed through fa_fwd_varlen run the ping-pong
+    kernel on the same rows, in the same order, as fa_fwd on [b, h, s, d]
+    (per-pair grid, not the persistent one): the results are bitwise equal."""
+    import torch
+    note(f"[parity-varlen-pp] b2 h64 s2048 d128 bf16 causal={causal}")
+    cfg = fa.fa_query_config(2, 128, int(causal), 2, 64, 2048, 2048)
+    assert (cfg["waves"], cfg["block_m"]) == (8, 256)
+    assert not fa.fa_query_launch(2, 128, int(causal), 2, 64, 2048, 2048)["persistent"]
+    w = W.shape("vlpp", "bf16", 2, 64, 2048, 2048, 128, causal, seed=77)
+    q, k, v = (t.cuda() for t in W.make(w))
+    o, lse = fa.attention(q, k, v, causal=causal)
+    pack = lambda t: t.permute(1, 0, 2, 3).reshape(64, 2 * 2048, 128).contiguous()
+    cu = torch.tensor([0, 2048, 4096], dtype=torch.int32, device="cuda")
+    ov, lv = fa.attention_varlen(pack(q), pack(k), pack(v), cu, cu, 2048, causal=causal)
+    torch.cuda.synchronize()
+    assert torch.equal(ov, pack(o))
+    assert torch.equal(lv, lse.permute(1, 0, 2).reshape(64, 4096))

@@ -62,6 +62,8 @@ def test_poisoned_varlen(gpu):
     with fa.poisoned():
         P.test_varlen_per_sequence_compare(("bf16", 2, 128, True, (300, 17, 130), (300, 40, 129)), gpu)
         P.test_varlen_per_sequence_compare(("bf16", 2, 128, True, (700, 1, 1500), (900, 300, 1500)), gpu)
+        P.test_varlen_per_sequence_compare(("bf16", 32, 128, True, (700, 1, 1500, 2048, 300, 4000),
+                                            (900, 300, 1500, 2048, 300, 3000)), gpu)
 
 
 def test_poisoned_backward(gpu):

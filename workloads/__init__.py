@@ -89,6 +89,13 @@ def shape(name: str = "custom", dtype: str = "bf16", b: int = 1, h: int = 1,
     return Workload(name, dtype, b, h, sq, sk, d, causal, scale, seed, qk_mult, v_dist)
 
 
+def varlen_lengths(n: int, lo: int, hi: int, seed: int):
+    """Lengths of n packed sequences for a variable-length batch: i.i.d.
+    integers uniform on [lo, hi] from numpy.random.default_rng(seed)."""
+    rng = np.random.default_rng(seed)
+    return [int(x) for x in rng.integers(lo, hi + 1, n)]
+
+
 def _torch_dtype(dtype: str):
     import torch
     return {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dtype]
