@@ -398,17 +398,17 @@ FA_API int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, f
     // fa_fwd does
     const int64_t live_items = h * ((total_q + tc.block_m - 1) / tc.block_m + batch);
     int mode = (d <= 128 && live_items < 256 && total_k >= 4 * (int64_t)tc.block_n * batch) ? 1 : 0;
-    // d = 128, at most 64 sequences of 1024 query rows or more on average,
-    // and at least one ping-pong work item per CU (counted on whole 256-row
-    // tiles, two per causal pair), as fa_fwd: the 8-wave ping-pong kernel, one
-    // work item per (head, sequence, causal pair or query tile), cost-ordered
-    // in the kernel; the grid covers the longest sequence's item count for
-    // every sequence and the rest exit.  Measured at h = 32 against the
+    // d = 128, h a multiple of 8 (equal work per XCD), at most 64 sequences
+    // of 1024 query rows or more on average, and at least one ping-pong work
+    // item per CU (counted on whole 256-row tiles, two per causal pair), as
+    // fa_fwd: the 8-wave ping-pong kernel, one work item per (head, sequence,
+    // causal pair or query tile), ordered in the kernel; the grid covers the
+    // longest sequence's item count for every sequence and the rest exit.  Measured at h = 32 against the
     // 4-wave kernel: equal lengths of 1024-4096 4-12 % faster, mixed lengths
     // of mean 1200-6800 within +-4 %, 64 sequences of mean 650 8-9 % slower
     // (256-row tiles leave more rows idle on short sequences).
     p.batch = (int)batch;
-    if (d == 128 && batch <= 64 && total_q >= 1024 * batch &&
+    if (d == 128 && h % 8 == 0 && batch <= 64 && total_q >= 1024 * batch &&
         h * (total_q / 256) / (causal ? 2 : 1) >= 256) {
         const int64_t t256 = (max_sq + 255) / 256;
         const int64_t per_seq = causal ? (t256 + 1) / 2 : t256;

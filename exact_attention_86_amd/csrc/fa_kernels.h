@@ -90,7 +90,7 @@ bool tile_config(int dtype, int d, int64_t bh, int64_t sq, int64_t sk, int causa
 hipError_t launch_fwd(int dtype, int d, const TileConfig& tc, const Params& p, hipStream_t stream);
 bool tile_config_split(int dtype, int d, TileConfig* tc);
 // mode 0: the 4-wave kernel; 1: with two key groups (d <= 128); 2: the
-// ping-pong kernel (d = 128, at most 64 sequences; the grid covers
+// ping-pong kernel (d = 128, h a multiple of 8, at most 64 sequences; the grid covers
 // h * batch * (items of the longest sequence), cost-ordered, the rest exit)
 hipError_t launch_fwd_varlen(int dtype, int d, const Params& p, int mode, hipStream_t stream);
 hipError_t launch_fwd_fp8(const Fp8Params& p, hipStream_t stream);

@@ -277,13 +277,13 @@ def test_deterministic(b, h, sq, waves, block_m, gpu):
 
 def four_wave_head_chunk(h, sq, sk, causal):
     """Heads per fa_fwd_varlen call (a divisor of h) for which a one-sequence
-    call keeps the plain 4-wave kernel: fewer than 1024 rows or fewer than
-    256 ping-pong items (h * floor(sq / 256), halved when causal) and, unless
+    call keeps the plain 4-wave kernel: fewer than 1024 rows, a head count
+    that is not a multiple of 8, or fewer than 256 ping-pong items (h * floor(sq / 256), halved when causal) and, unless
     the keys span fewer than 4 tiles of 64, at least 256 row tiles
     (h * (ceil(sq / 128) + 1)), so that neither the ping-pong kernel nor two
     key groups are chosen."""
     def plain(c):
-        pp = sq >= 1024 and c * (sq // 256) // (2 if causal else 1) >= 256
+        pp = sq >= 1024 and c % 8 == 0 and c * (sq // 256) // (2 if causal else 1) >= 256
         kg = c * (-(-sq // 128) + 1) < 256 and sk >= 4 * 64
         return not pp and not kg
     return max(c for c in range(1, h + 1) if h % c == 0 and plain(c))
@@ -405,16 +405,16 @@ VARLEN = [
     # long keys, few tiles: two key groups per tile (8 waves)
     ("bf16", 2, 128, True, [700, 1, 1500], [900, 300, 1500]),
     ("f16", 2, 64, False, [333, 1000], [1200, 2000]),
-    # d = 128, sequences of 1024 rows or more on average and a ping-pong work
-    # item per CU: the 8-wave ping-pong kernel, one item per (head, sequence,
+    # d = 128, h a multiple of 8, sequences of 1024 rows or more on average and
+    # a ping-pong work item per CU: the 8-wave ping-pong kernel, one item per (head, sequence,
     # causal pair); sq > sk and sq < sk, a single row, a sequence shorter than
     # one 256-row tile
     ("bf16", 32, 128, True, [700, 1, 1500, 2048, 300, 4000], [900, 300, 1500, 2048, 300, 3000]),
     ("f16", 16, 128, False, [1000, 2500, 1500, 129, 1, 1500], [1000, 2600, 1500, 1, 77, 1500]),
     # 64 sequences: the ping-pong kernel's limit (one lane per sequence when it
     # ranks them by cost); 65: the 4-wave kernel
-    ("bf16", 4, 128, False, [1000 + 13 * i for i in range(64)], [1000 + 13 * i for i in range(64)]),
-    ("f16", 4, 128, True, [1000 + 9 * i for i in range(65)], [1000 + 9 * i for i in range(65)]),
+    ("bf16", 8, 128, False, [1000 + 13 * i for i in range(64)], [1000 + 13 * i for i in range(64)]),
+    ("f16", 8, 128, True, [1000 + 9 * i for i in range(65)], [1000 + 9 * i for i in range(65)]),
 ]
 
 
