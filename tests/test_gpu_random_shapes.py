@@ -58,7 +58,36 @@ def draw_many_heads(seed, n):
     return cases
 
 
+def draw_packed(seed, n):
+    """Packed batches that take the ping-pong kernel's variable-length form:
+    d = 128, h a multiple of 8, 2-64 sequences averaging at least 1024 query
+    rows, enough 256-row tiles for a work item per CU.  Query and key lengths
+    are drawn apart (sq < sk and sq > sk, equal lengths, so equal costs,
+    single rows, and sequences without queries or keys)."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        dt = str(rng.choice(["f16", "bf16"]))
+        h = int(rng.choice([8, 16, 32]))
+        nb = int(rng.integers(2, 65))
+        causal = bool(rng.integers(0, 2))
+        base = int(rng.integers(1024, 2600))
+        ql = [int(x) for x in rng.integers(1, 2 * base, nb)]
+        kl = [int(x) if rng.random() < 0.6 else ql[i] for i, x in enumerate(rng.integers(1, 2 * base, nb))]
+        if nb > 3:
+            ql[1] = ql[2]  # a tie in the cost ranking
+            kl[1] = kl[2]
+            ql[3], kl[0] = 0, 0  # no queries; no keys
+        tq = sum(ql)
+        work = sum(h * a * b * 128 * 4 for a, b in zip(ql, kl))
+        if tq < 1024 * nb or h * (tq // 256) // (2 if causal else 1) < 256 or work > 4e11:
+            continue
+        cases.append((dt, h, causal, ql, kl, 8100 + len(cases)))
+    return cases
+
+
 FWD = draw_cases(11, 16, True) + draw_many_heads(13, 6)
+PACKED = draw_packed(14, 6)
 BWD = draw_cases(12, 10, False)
 ids = lambda c: "%s-b%dh%d-sq%d-sk%d-d%d-%s" % (c[0], c[1], c[2], c[3], c[4], c[5], "causal" if c[6] else "full")
 
@@ -99,3 +128,38 @@ def test_random_backward(case):
     check("dq", dq, rq, dt)
     check("dk", dk, rk, dt)
     check("dv", dv, rv, dt)
+
+
+@pytest.mark.parametrize("case", PACKED, ids=lambda c: "%s-h%d-%s-%dseqs" % (c[0], c[1], "causal" if c[2] else "full", len(c[3])))
+def test_random_packed_forward(case):
+    """Every sequence of a random packed batch against the oracle on that
+    sequence alone (the rows of a sequence without keys are not written)."""
+    import torch
+    dt, h, causal, ql, kl, seed = case
+    note(f"[random-packed] {dt} h{h} causal={causal} q={ql} k={kl}")
+    qs, ks, vs = [], [], []
+    for i, (a, b) in enumerate(zip(ql, kl)):
+        w = W.shape("rndp%d" % i, dt, 1, h, max(a, 1), max(b, 1), 128, causal, seed=seed * 100 + i)
+        q, k, v = W.make(w)
+        qs.append(q[0, :, :a])
+        ks.append(k[0, :, :b])
+        vs.append(v[0, :, :b])
+    cat = lambda xs: torch.cat(xs, dim=1).contiguous()
+    qp, kp, vp = cat(qs), cat(ks), cat(vs)
+    cq = np.concatenate([[0], np.cumsum(ql)]).astype(np.int32)
+    ck = np.concatenate([[0], np.cumsum(kl)]).astype(np.int32)
+    s = scale32(1.0 / math.sqrt(128))
+    o, lse = fa.attention_varlen(qp.cuda(), kp.cuda(), vp.cuda(), torch.from_numpy(cq).cuda(),
+                                 torch.from_numpy(ck).cuda(), max(ql), causal=causal, scale=s)
+    torch.cuda.synchronize()
+    go, gl = o.double().cpu().numpy(), lse.double().cpu().numpy()
+    worst_o = worst_l = 0.0
+    for i in range(len(ql)):
+        if ql[i] == 0 or kl[i] == 0:
+            continue
+        q0, q1, k0, k1 = cq[i], cq[i + 1], ck[i], ck[i + 1]
+        ro, rl = oracle.attn(qp[None, :, q0:q1], kp[None, :, k0:k1], vp[None, :, k0:k1], s, causal)
+        worst_o = max(worst_o, float(np.max(np.abs(go[:, q0:q1] - ro[0]))))
+        worst_l = max(worst_l, float(np.max(np.abs(gl[:, q0:q1] - rl[0]))))
+    note(f"   O max-abs {worst_o:.3e}, LSE max-abs {worst_l:.3e}")
+    assert worst_o <= TOL_O[dt] and worst_l <= TOL_LSE
