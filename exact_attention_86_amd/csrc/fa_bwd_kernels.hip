@@ -235,16 +235,18 @@ fa_bwd_dkdv(BwdParams p)
     };
     // LSE (converted to log2 units) and D of a step's 64 rows: wave 0 fetches
     // LSE, wave 1 fetches D, one row per lane, and writes them into the stage
-    // just before the barrier that publishes it
+    // just before the barrier that publishes it.  The conversion happens at
+    // the store, so no wave waits for the load before its matrix-core work
+    // (the copy wait before that barrier covers it).
     float pend = 0.f;
     auto fetch_rows = [&](int q0) {
         if (w < 2) {
             const int r = min(q0 + lane, sq - 1);
-            pend = (w == 0) ? LSE[r] * kLog2e : DV[r];
+            pend = (w == 0) ? LSE[r] : DV[r];
         }
     };
     auto store_rows = [&](int st) {
-        if (w < 2) *(float*)(lds + st * STAGE + OFF_LSE + w * BMQ * 4 + lane * 4) = pend;
+        if (w < 2) *(float*)(lds + st * STAGE + OFF_LSE + w * BMQ * 4 + lane * 4) = (w == 0) ? pend * kLog2e : pend;
     };
 
     // ---- per-lane LDS read offsets (bytes within a stage) ----
