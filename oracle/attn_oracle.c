@@ -16,7 +16,7 @@
  * times softmax_scale, then exp(score - row max)).  The row log-sum-exp is
  * reported as LSE_i = m_i + ln(l_i) in natural-log units.
  *
- * Readings taken where the pages are silent (each is listed in the design doc):
+ * Readings taken where the pages are silent:
  *   - causal mask: key j is allowed for query i iff j <= i (top-left
  *     alignment; identical to bottom-right when sq == sk);
  *   - keys j >= sk do not exist (ragged lengths contribute nothing);
