@@ -49,8 +49,8 @@
  *
  * All arrays are fp64, contiguous, row-major: q,o [b,h,sq,d]; k,v [b,h,sk,d];
  * lse [b,h,sq].  Return value 0 on success, -1 on invalid arguments.
- * The online forms are parity unpinned against the pages' numbers (the pages
- * print none); they are pinned to the naive form by brute force.
+ * The pages print no worked values for the online forms; their pins are the
+ * plain definition above, by brute force over small shapes and tile sizes.
  */
 #include <math.h>
 #include <pthread.h>
